@@ -1,0 +1,368 @@
+// C ABI of the fused MoE layer (declared in include/moe.h).
+//
+// Argument rules follow the DeepGEMM MegaMoE experts page:
+// check_deep_gemm_mega_moe_supported (hidden and intermediate multiples of
+// 128, else ValueError; unsupported device, NotImplementedError),
+// MegaMoEActivation (finite alpha/beta, clamp >= 0; unsupported activation,
+// NotImplementedError), DeepGemmMegaMoEExperts.forward (more tokens than the
+// buffer was sized for, ValueError).  Every check runs before anything is
+// enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+struct DeviceInfo {
+  bool checked = false;
+  bool gfx950 = false;
+  int cus = 0;
+  bool gemm_ready = false;
+};
+constexpr int MAX_DEVICES = 64;
+DeviceInfo g_dev[MAX_DEVICES];
+std::mutex g_mu;
+thread_local hipError_t g_last_hip = hipSuccess;
+
+// Returns MOE_OK and fills *info for the current device, or an error.
+int device_info(DeviceInfo** info) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { g_last_hip = e; return MOE_E_UNSUPPORTED; }
+  if (dev < 0 || dev >= MAX_DEVICES) return MOE_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) { g_last_hip = e; return MOE_E_UNSUPPORTED; }
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.gfx950) return MOE_E_UNSUPPORTED;
+  if (!d.gemm_ready) {
+    e = gemm_init(dev);
+    if (e != hipSuccess) { g_last_hip = e; return MOE_E_HIP; }
+    d.gemm_ready = true;
+  }
+  *info = &d;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carve-up of moe_forward.
+struct Workspace {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* meta;
+  int32_t* sorted_slot;
+  int32_t* slot_row;
+  int32_t* tile_expert;
+  uint8_t* xq;        // dispatch-quantised x codes
+  uint8_t* xq_sf;     // its block scales
+  float* x_tok;       // NVFP4 per-token scale
+  uint8_t* a2;        // L2 input codes
+  uint8_t* a2_sf;     // L2 input block scales
+  float* o;           // L2 output rows per slot
+  size_t bytes;
+};
+
+Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t n_sh, int64_t k, int64_t bm,
+               uint8_t* base) {
+  const int64_t E = n_loc + n_sh, S = T * (k + n_sh), M = S + E * (bm - 1);
+  Workspace w;
+  size_t off = 0;
+  auto take = [&](size_t n) { uint8_t* p = base ? base + off : nullptr; off += align_up(n); return p; };
+  w.counts = (int32_t*)take(E * 4);
+  w.offsets = (int32_t*)take((E + 1) * 4);
+  w.meta = (int32_t*)take(16);
+  w.sorted_slot = (int32_t*)take(M * 4);
+  w.slot_row = (int32_t*)take(S * 4);
+  w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
+  w.xq = w.xq_sf = w.a2 = w.a2_sf = nullptr;
+  w.x_tok = nullptr;
+  if (fmt == F_MXFP8 || fmt == F_MXFP4) {
+    w.xq = take(T * H);
+    w.xq_sf = take(T * H / 32);
+    w.a2 = take(M * I);
+    w.a2_sf = take(M * I / 32);
+  } else if (fmt == F_NVFP4) {
+    w.xq = take(T * H / 2);
+    w.xq_sf = take(T * H / 16);
+    w.x_tok = (float*)take(T * 4);
+    w.a2 = take(M * I / 2);
+    w.a2_sf = take(M * I / 16);
+  } else {
+    w.a2 = take(M * I * 2);
+  }
+  w.o = (float*)take(S * H * 4);
+  w.bytes = off;
+  return w;
+}
+
+bool valid_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == MOE_FMT_MXFP4 || f == MOE_FMT_NVFP4; }
+
+// Formats whose grouped GEMMs this build implements.
+bool gemm_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == MOE_FMT_MXFP4; }
+
+int block_m_rule(int T, int n_loc, int n_sh, int k) {
+  const double expected = (double)T * (k + n_sh) / (double)(n_loc + n_sh);
+  if (expected <= 32) return 32;
+  if (expected <= 64) return 64;
+  if (expected <= 128) return 128;
+  return 256;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = e;
+  return MOE_E_HIP;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_E_INVALID: return "invalid argument";
+    case MOE_E_UNSUPPORTED: return "unsupported device, format or activation";
+    case MOE_E_WORKSPACE: return "workspace too small";
+    case MOE_E_HIP: return g_last_hip == hipSuccess ? "HIP error" : hipGetErrorString(g_last_hip);
+    default: return "unknown status";
+  }
+}
+
+int moe_get_block_m(int num_tokens, int num_local_experts, int num_shared, int top_k, moe_format_t fmt) {
+  if (num_tokens < 0 || num_local_experts < 1 || num_shared < 0 || top_k < 1 || !valid_fmt(fmt)) return MOE_E_INVALID;
+  return block_m_rule(num_tokens, num_local_experts, num_shared, top_k);
+}
+
+size_t moe_workspace_bytes(moe_format_t fmt, int max_tokens, int hidden, int inter, int num_local_experts,
+                           int num_shared, int top_k, int block_m) {
+  if (!valid_fmt(fmt) || max_tokens < 0 || hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128 ||
+      num_local_experts < 1 || num_shared < 0 || top_k < 1)
+    return 0;
+  if (block_m == 0) block_m = 256;
+  if (block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return 0;
+  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, nullptr).bytes;
+}
+
+int moe_transform_weights(moe_format_t fmt, int num_experts, int hidden, int inter, const void* w13,
+                          const void* w13_sf, const void* w2, const void* w2_sf, void* w13_k, void* w13_sf_k,
+                          void* w2_k, void* w2_sf_k, void* stream) {
+  if (!valid_fmt(fmt) || num_experts < 1 || hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128)
+    return MOE_E_INVALID;
+  if (!w13 || !w2 || !w13_k || !w2_k || !aligned16(w13) || !aligned16(w2) || !aligned16(w13_k) || !aligned16(w2_k))
+    return MOE_E_INVALID;
+  const bool scaled = fmt != MOE_FMT_BF16;
+  if (scaled && (!w13_sf || !w2_sf || !w13_sf_k || !w2_sf_k)) return MOE_E_INVALID;
+  if (!gemm_fmt(fmt)) return MOE_E_UNSUPPORTED;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  launch_transform(fmt, num_experts, hidden, inter, (const uint8_t*)w13, (const uint8_t*)w13_sf, (const uint8_t*)w2,
+                   (const uint8_t*)w2_sf, (uint8_t*)w13_k, (uint8_t*)w13_sf_k, (uint8_t*)w2_k, (uint8_t*)w2_sf_k,
+                   (hipStream_t)stream);
+  return hip_status(hipGetLastError());
+}
+
+int moe_quantize_weights(moe_format_t fmt, int num_experts, int rows, int cols, const float* src, void* codes,
+                         void* scales, float* gscale, void* stream) {
+  if (!(fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_NVFP4)) return MOE_E_INVALID;
+  if (num_experts < 1 || rows < 1 || cols < 32 || cols % 32) return MOE_E_INVALID;
+  if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes)) return MOE_E_INVALID;
+  if (fmt == MOE_FMT_NVFP4 && !gscale) return MOE_E_INVALID;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = (int64_t)num_experts * rows;
+  if (fmt == MOE_FMT_NVFP4) {
+    launch_weight_gscale(num_experts, (int64_t)rows * cols, src, gscale, s);
+    launch_quant_nv(true, R, cols, src, (uint8_t*)codes, (uint8_t*)scales, nullptr, gscale, rows, s);
+  } else {
+    launch_quant_mx(fmt == MOE_FMT_MXFP4, true, R, cols, src, (uint8_t*)codes, (uint8_t*)scales, s);
+  }
+  return hip_status(hipGetLastError());
+}
+
+int moe_quantize_x(moe_format_t fmt, int num_tokens, int hidden, const void* x, void* codes, void* scales,
+                   float* token_scale, void* stream) {
+  if (!(fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_NVFP4)) return MOE_E_INVALID;
+  if (num_tokens < 0 || hidden < 32 || hidden % 32) return MOE_E_INVALID;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_E_INVALID;
+  if (fmt == MOE_FMT_NVFP4 && !token_scale) return MOE_E_INVALID;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == MOE_FMT_NVFP4)
+    launch_quant_nv(false, num_tokens, hidden, x, (uint8_t*)codes, (uint8_t*)scales, token_scale, nullptr, 1, s);
+  else
+    launch_quant_mx(false, false, num_tokens, hidden, x, (uint8_t*)codes, (uint8_t*)scales, s);
+  return hip_status(hipGetLastError());
+}
+
+int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start, int num_local_experts, int block_m,
+                 const int32_t* topk_ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                 int32_t* tile_expert, void* stream) {
+  if (num_tokens < 0 || top_k < 1 || num_shared < 0 || num_local_experts < 1 ||
+      num_local_experts + num_shared > MAX_LOCAL_EXPERTS)
+    return MOE_E_INVALID;
+  if (block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return MOE_E_INVALID;
+  if ((num_tokens > 0 && top_k > 0 && !topk_ids) || !counts || !offsets || !sorted_slot || !slot_row || !tile_expert)
+    return MOE_E_INVALID;
+  if ((int64_t)num_tokens * (top_k + num_shared) > (int64_t)1 << 30) return MOE_E_INVALID;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, block_m, counts, offsets,
+                  sorted_slot, slot_row, tile_expert, nullptr, (hipStream_t)stream);
+  return hip_status(hipGetLastError());
+}
+
+int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
+                         int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
+                         const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
+                         const void* w13_sf_k, const void* w2_k, const void* w2_sf_k, const float* w13_gscale,
+                         const float* w2_gscale, float l2_activation_scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* ev) {
+  // ---- shapes and parameters
+  if (!valid_fmt(fmt)) return MOE_E_INVALID;
+  if (num_tokens < 0 || hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128) return MOE_E_INVALID;
+  if (top_k < 1 || num_local_experts < 1 || num_shared < 0 || num_local_experts + num_shared > MAX_LOCAL_EXPERTS)
+    return MOE_E_INVALID;
+  if ((int64_t)num_tokens * (top_k + num_shared) > (int64_t)1 << 30) return MOE_E_INVALID;
+  if (block_m != 0 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return MOE_E_INVALID;
+  moe_activation_t a = {MOE_ACT_SWIGLU, 0, 0.0f, 1.0f, 0.0f};
+  if (act) a = *act;
+  if (a.kind != MOE_ACT_SWIGLU) return MOE_E_UNSUPPORTED;
+  if (!isfinite(a.alpha) || !isfinite(a.beta) || (a.has_clamp && !(a.clamp >= 0.0f))) return MOE_E_INVALID;
+  if (fmt == MOE_FMT_NVFP4 && (!(l2_activation_scale > 0.0f) || !isfinite(l2_activation_scale)))
+    return MOE_E_INVALID;
+  if (num_tokens == 0) return MOE_OK;
+  // ---- pointers
+  const bool scaled = fmt != MOE_FMT_BF16;
+  if (!x || !topk_ids || !topk_weights || !w13_k || !w2_k || !out || !workspace) return MOE_E_INVALID;
+  if (!aligned16(x) || !aligned16(w13_k) || !aligned16(w2_k) || !aligned16(out) || !aligned16(workspace))
+    return MOE_E_INVALID;
+  if (scaled && (!w13_sf_k || !w2_sf_k || !aligned16(w13_sf_k) || !aligned16(w2_sf_k))) return MOE_E_INVALID;
+  if (fmt == MOE_FMT_NVFP4 && (!w13_gscale || !w2_gscale)) return MOE_E_INVALID;
+  if (!gemm_fmt(fmt) || hidden % 256) return MOE_E_UNSUPPORTED;
+  const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k);
+  const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
+  const int E = num_local_experts + num_shared;
+  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, nullptr).bytes > workspace_bytes)
+    return MOE_E_WORKSPACE;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, (uint8_t*)workspace);
+  auto mark = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+  };
+
+  // a1: dispatch quantisation
+  mark(2 * MOE_STEP_QUANT_X);
+  if (fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4)
+    launch_quant_mx(false, false, T, (int)H, x, w.xq, w.xq_sf, s);
+  mark(2 * MOE_STEP_QUANT_X + 1);
+  // a2: routing metadata
+  mark(2 * MOE_STEP_DISPATCH);
+  launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts, w.offsets,
+                  w.sorted_slot, w.slot_row, w.tile_expert, w.meta, s);
+  mark(2 * MOE_STEP_DISPATCH + 1);
+  const int grid = (d->cus >= 8 ? d->cus : 8) / 8 * 8;
+
+  // a3-a5: L1 GEMM + activation + L2-input quantisation
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  const int64_t ebytes = fmt == MOE_FMT_BF16 ? 2 : 1;  // bytes per element (codes); FP4 below
+  if (fmt == MOE_FMT_BF16) {
+    g.a = (const uint8_t*)x;
+    g.a_ld = H * 2;
+  } else {
+    g.a = w.xq;
+    g.a_ld = H;
+    g.a_sf = w.xq_sf;
+    g.a_sf_ld = H / 32;
+  }
+  g.w = (const uint8_t*)w13_k;
+  g.w_sf = (const uint8_t*)w13_sf_k;
+  const int64_t w13_elems = 2 * I * H, w2_elems = H * I;
+  g.w_expert_bytes = fmt == MOE_FMT_MXFP4 ? w13_elems / 2 : w13_elems * ebytes;
+  g.w_sf_expert_bytes = scaled ? w13_elems / 32 : 0;
+  g.N = (int)(2 * I);
+  g.K = (int)H;
+  g.sorted_slot = w.sorted_slot;
+  g.offsets = w.offsets;
+  g.meta = w.meta;
+  g.num_experts = E;
+  g.kk = (int)kk;
+  g.c = w.a2;
+  g.c_sf = w.a2_sf;
+  g.c_ld = fmt == MOE_FMT_BF16 ? I * 2 : I;
+  g.c_sf_ld = I / 32;
+  g.inter = (int)I;
+  g.has_clamp = a.has_clamp;
+  g.clamp = a.clamp;
+  g.alpha = a.alpha;
+  g.beta = a.beta;
+  g.l2_scale = l2_activation_scale;
+  mark(2 * MOE_STEP_L1);
+  hipError_t e = launch_gemm(fmt, 1, bm, g, grid, s);
+  if (e != hipSuccess) return hip_status(e);
+  mark(2 * MOE_STEP_L1 + 1);
+
+  // a6: L2 GEMM
+  GemmArgs g2 = g;
+  g2.a = w.a2;
+  g2.a_ld = g.c_ld;
+  g2.a_sf = w.a2_sf;
+  g2.a_sf_ld = I / 32;
+  g2.w = (const uint8_t*)w2_k;
+  g2.w_sf = (const uint8_t*)w2_sf_k;
+  g2.w_expert_bytes = fmt == MOE_FMT_MXFP4 ? w2_elems / 2 : w2_elems * ebytes;
+  g2.w_sf_expert_bytes = scaled ? w2_elems / 32 : 0;
+  g2.N = (int)H;
+  g2.K = (int)I;
+  g2.o = w.o;
+  mark(2 * MOE_STEP_L2);
+  e = launch_gemm(fmt, 2, bm, g2, grid, s);
+  if (e != hipSuccess) return hip_status(e);
+  mark(2 * MOE_STEP_L2 + 1);
+
+  // a7: weighted combine
+  mark(2 * MOE_STEP_COMBINE);
+  launch_combine(w.o, w.slot_row, topk_weights, num_tokens, top_k, (int)kk, (int)H, (uint16_t*)out, s);
+  mark(2 * MOE_STEP_COMBINE + 1);
+  return hip_status(hipGetLastError());
+}
+
+int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
+                int num_local_experts, int num_shared, int block_m, const moe_activation_t* act, const void* x,
+                const int32_t* topk_ids, const float* topk_weights, const void* w13_k, const void* w13_sf_k,
+                const void* w2_k, const void* w2_sf_k, const float* w13_gscale, const float* w2_gscale,
+                float l2_activation_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_profiled(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,
+                              block_m, act, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale,
+                              w2_gscale, l2_activation_scale, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Shared device/host definitions of the MI355X (gfx950) fused-MoE library.
+//
+// Number formats (DeepGEMM MegaMoE experts page, module docstring and
+// MegaMoEWeightSpec; element encodings of the OCP FP8 and OCP MX v1.0
+// specifications): BF16; FP8 E4M3 (bias 7, max 448, no inf); FP4 E2M1
+// (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; two per byte, even element in the
+// low nibble); UE8M0 block scales (a biased exponent; the Qwen4-Exp MegaMoE
+// page's _requantize moves it into / out of the float32 exponent field);
+// E4M3 block scales with a float32 global scale (NVFP4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- vectors
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- shapes
+// Layer-level constants of the formats.
+constexpr int MX_GROUP = 32;   // UE8M0 scale per 32 values along K
+constexpr int NV_GROUP = 16;   // E4M3 scale per 16 values along K
+
+// Kernel-layout fragment geometry.  A weight fragment is 32 rows (N) x one
+// MFMA K-step, stored as 64 lanes x 16 bytes in the order the MFMA operand
+// registers want them (lane l: row l % 32, second K-half when l >= 32).
+//   BF16: 32x32x16 MFMA, K-step 16 elements = 32 bytes per row, 1 KiB/frag.
+//   FP8:  32x32x64 scaled MFMA, K-step 64 elements = 64 bytes/row, 2 KiB.
+//   FP4:  32x32x64 scaled MFMA, K-step 64 elements = 32 bytes/row, 1 KiB.
+// w13 rows are interleaved in 32-row blocks: kernel row n -> pair p = n / 64,
+// half h = (n / 32) % 2 (0 gate, 1 up), canonical row h * I + p * 32 + n % 32.
+__host__ __device__ inline int w13_canonical_row(int n, int inter) {
+  return ((n >> 5) & 1) * inter + (n >> 6) * 32 + (n & 31);
+}
+
+// ---------------------------------------------------------------- bits
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = f2u(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- E4M3 / E2M1
+// Round-to-nearest-even, saturating to the largest finite magnitude; the
+// code's sign bit is the input's sign bit.  All steps are exact in float32:
+// a power-of-two scaling, an exact subtraction, and rint (ties to even).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+#pragma clang fp contract(off)
+  uint32_t sign = (f2u(x) >> 24) & 0x80u;
+  float a = __builtin_fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                         // below 2^-6: step 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  int e = (int)((f2u(a) >> 23) & 0xFF) - 127;  // 2^-6 <= a < 448 -> e in [-6, 8]
+  float m = __builtin_ldexpf(a, -e);           // [1, 2)
+  uint32_t q = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);
+  if (q == 8u) { q = 0; e += 1; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | q;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+#pragma clang fp contract(off)
+  uint32_t sign = (f2u(x) >> 28) & 0x8u;
+  float a = __builtin_fabsf(x);
+  if (!(a < 8.0f)) return sign | 0x7u;
+  if (a < 1.0f) return sign | (uint32_t)__builtin_rintf(a * 2.0f);  // 0, 0.5, 1
+  int e = (int)((f2u(a) >> 23) & 0xFF) - 127;  // 0..2
+  float m = __builtin_ldexpf(a, -e);
+  uint32_t q = (uint32_t)__builtin_rintf((m - 1.0f) * 2.0f);
+  if (q == 2u) { q = 0; e += 1; }
+  if (e > 2) return sign | 0x7u;
+  return sign | ((uint32_t)(e + 1) << 1) | q;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t E = (c >> 3) & 0xF, M = c & 7;
+  float mag = E == 0 ? (float)M * 0.001953125f : __builtin_ldexpf(1.0f + (float)M * 0.125f, (int)E - 7);
+  return (c & 0x80) ? -mag : mag;
+}
+
+// UE8M0 code of an MX block from its float32 amax (> 0): the smallest e with
+// amax <= fmax * 2^e, code 127 + e clamped to [1, 254].  With amax = m * 2^p:
+// E4M3 (fmax = 1.75 * 2^8): e = p - 8 + [m > 1.75];  E2M1 (1.5 * 2^2):
+// e = p - 2 + [m > 1.5].  A subnormal amax always clamps to 1.
+template <bool FP4>
+__device__ __forceinline__ int mx_scale_code(float amax) {
+  uint32_t u = f2u(amax);
+  int E = (int)(u >> 23);
+  uint32_t M = u & 0x7FFFFFu;
+  if (E == 0) return 1;
+  int c = FP4 ? E - 2 + (M > 0x400000u) : E - 8 + (M > 0x600000u);
+  return c < 1 ? 1 : (c > 254 ? 254 : c);
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+// max over the 2^LOG lanes of a lane group (group = lanes with equal l >> LOG)
+template <int LOG>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = 1; m < (1 << LOG); m <<= 1) v = __builtin_fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte global -> LDS copy without a register round trip: lane l's 16
+// bytes land at `lds_base + 16 * l` (lds_base is uniform over the wave).
+__device__ __forceinline__ void g2lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 0);
+}
+
+}  // namespace moe

@@ -1,0 +1,144 @@
+// Token dispatch: routing metadata for the grouped GEMMs.
+//
+// The contiguous layout of the "fused_moe" page's DeepGemmExperts.apply:
+// rows of every local expert are gathered into one group padded to BLOCK_M
+// (compute_aligned_M), permuted there and un-permuted after the L2 GEMM.
+// Slot s = t * k' + j (k' = top_k + num_shared); shared choices are always
+// selected (DeepGEMM MegaMoE experts page: a fused shared expert runs inside
+// the launch as an always-selected expert); routed ids outside this GPU's
+// expert range are dropped.
+//
+// One workgroup of 16 waves.  Wave w owns a contiguous run of slots.  Pass 1
+// counts each expert's slots per wave: inside a 64-slot batch the lanes that
+// hold the same expert find each other with one ballot per expert-id bit, and
+// the lowest such lane adds the group size, so no two lanes of a wave touch
+// one counter and no order-dependent atomics are needed.  Pass 2 scans the
+// per-wave counts (per expert) and the BLOCK_M-padded totals (over experts).
+// Pass 3 walks the batches again in order and scatters every slot to
+// offset + (earlier slots of its expert), which is the stable order.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int DISPATCH_WAVES = 16;
+constexpr int DISPATCH_THREADS = DISPATCH_WAVES * WAVE;
+
+__device__ __forceinline__ int slot_expert(const int32_t* __restrict__ topk_ids, int s, int kk, int k,
+                                           int start, int n_loc) {
+  int t = s / kk, j = s - t * kk;
+  if (j >= k) return n_loc + (j - k);
+  int e = topk_ids[(size_t)t * k + j] - start;
+  return (e >= 0 && e < n_loc) ? e : -1;
+}
+
+// Lanes of this wave whose expert equals mine (bit-sliced compare).
+__device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
+  uint64_t m = ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    bool bit = (e >> b) & 1;
+    uint64_t bb = ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return e >= 0 ? m : 0ull;
+}
+
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc,
+           int bm, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+           int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+           int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+  __shared__ int hist[DISPATCH_WAVES][MAX_LOCAL_EXPERTS];
+  __shared__ int wave_tot[DISPATCH_WAVES];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+
+  for (int i = tid; i < DISPATCH_WAVES * MAX_LOCAL_EXPERTS; i += DISPATCH_THREADS) (&hist[0][0])[i] = 0;
+  __syncthreads();
+
+  // slots of wave w: [s0, s1), s0 a multiple of 64
+  const int per = ((S + DISPATCH_WAVES - 1) / DISPATCH_WAVES + WAVE - 1) / WAVE * WAVE;
+  const int s0 = min(w * per, S), s1 = min(s0 + per, S);
+
+  // pass 1: per-wave histogram
+  for (int b = s0; b < s1; b += WAVE) {
+    int s = b + l;
+    int e = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+    uint64_t m = match_mask(e, nbits);
+    if (e >= 0 && (__builtin_ctzll(m) == l)) hist[w][e] += __builtin_popcountll(m);
+  }
+  __syncthreads();
+
+  // pass 2a: expert tid: exclusive scan of its per-wave counts; padded size
+  static_assert(MAX_LOCAL_EXPERTS <= DISPATCH_THREADS, "one expert per thread");
+  int run = 0;
+  if (tid < E) {
+    for (int ww = 0; ww < DISPATCH_WAVES; ++ww) { int c = hist[ww][tid]; hist[ww][tid] = run; run += c; }
+    counts[tid] = run;
+  }
+  const int v = tid < E ? (run + bm - 1) / bm * bm : 0;
+  // pass 2b: exclusive scan of padded sizes over experts (one per thread)
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    int o = __shfl_up(incl, d, 64);
+    if (l >= d) incl += o;
+  }
+  if (l == WAVE - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int ww = 0; ww < w; ++ww) wbase += wave_tot[ww];
+  const int off = wbase + incl - v;                 // exclusive offset of expert tid
+  int total = 0;
+  for (int ww = 0; ww < DISPATCH_WAVES; ++ww) total += wave_tot[ww];
+  if (tid < E) {
+    offsets[tid] = off;
+    for (int ww = 0; ww < DISPATCH_WAVES; ++ww) hist[ww][tid] += off;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    if (meta) {
+      meta[0] = total / bm;   // number of BLOCK_M tiles
+      meta[1] = total;        // padded rows
+    }
+  }
+  __syncthreads();
+
+  // pass 3: stable scatter
+  for (int b = s0; b < s1; b += WAVE) {
+    int s = b + l;
+    bool live = s < s1;
+    int e = live ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+    uint64_t m = match_mask(e, nbits);
+    if (e >= 0) {
+      int pos = hist[w][e] + __builtin_popcountll(m & lt_mask);
+      sorted_slot[pos] = s;
+      slot_row[s] = pos;
+    } else if (live) {
+      slot_row[s] = -1;
+    }
+    // every lane has read its base before the group leader bumps it
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && __builtin_ctzll(m) == l) hist[w][e] += __builtin_popcountll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // padding rows and the tile -> expert table
+  if (tid < E) {
+    for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
+    for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
+  }
+}
+
+void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+                     int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                     int32_t* tile_expert, int32_t* meta, hipStream_t stream) {
+  int E = n_loc + n_sh;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh, start,
+                     n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta);
+}
+
+}  // namespace moe

@@ -1,0 +1,353 @@
+// Grouped expert GEMMs on gfx950 MFMA: L1 (x * W13^T, gated activation and
+// L2-input quantisation in the epilogue) and L2 (A2 * W2^T -> float32 rows
+// per slot).
+//
+// What is computed: the two expert GEMMs of the DeepGEMM MegaMoE experts page
+// (one launch runs L1, the activation of MegaMoEActivation, the L2-input
+// quantisation and L2), in the step order of the "fused_moe" page's
+// DeepGemmExperts.apply (grouped GEMM, activation, per-group quantisation,
+// grouped GEMM).  Weight formats: BF16 (32x32x16 bf16 MFMA), MXFP8 and MXFP4
+// (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4 consuming the UE8M0 block scales
+// directly; MXFP4 weights against MXFP8 activations).
+//
+// Work decomposition: a persistent grid of (#CUs) workgroups walks the tiles
+// (BLOCK_M rows of one expert x 256 output columns).  Every tile has the same
+// cost, so skewed routing only changes how many tiles an expert owns, and the
+// static round-robin stays balanced.  Tiles are ordered expert-major, then by
+// N block, then by M block, and each XCD takes a contiguous run of tiles per
+// round, so the M blocks of one expert that share a weight block run on the
+// same XCD at the same time and read it through that XCD's L2.
+//
+// Per tile: 4 waves, each owning a (BLOCK_M / WM) x (256 / WN) sub-tile of
+// 32x32 MFMA accumulators.  K advances in stages; each stage's A rows, weight
+// fragments and block scales are copied global -> LDS by the LDS-DMA path
+// (global_load_lds_dwordx4) into one of two buffers while the MFMAs consume
+// the other.  A rows sit in LDS as 128-byte rows whose 16-byte chunks are
+// XOR-swizzled by (row & 7), so the 8 lanes a ds_read_b128 services at once
+// hit 8 distinct bank groups.  Weights arrive in the kernel layout written by
+// moe_transform_weights: each 32-row x K-step fragment is 1 KiB (or 2 KiB)
+// in register order, so the weight copy and its LDS reads are linear.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+template <int FMT> struct FmtCfg;
+template <> struct FmtCfg<F_BF16> {
+  static constexpr int KSTAGE = 64, A_ROW = 128, B_ROW = 128, STEPS = 4;
+  static constexpr bool SCALED = false;
+};
+template <> struct FmtCfg<F_MXFP8> {
+  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 128, STEPS = 2;
+  static constexpr bool SCALED = true;
+};
+template <> struct FmtCfg<F_MXFP4> {
+  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 64, STEPS = 2;
+  static constexpr bool SCALED = true;
+};
+
+__device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
+  if (p.has_clamp) {
+    g = __builtin_fminf(g, p.clamp);
+    u = __builtin_fminf(__builtin_fmaxf(u, -p.clamp), p.clamp);
+  }
+  float s = __builtin_amdgcn_rcpf(1.0f + __expf(-p.alpha * g));
+  return g * s * (u + p.beta);
+}
+
+template <int FMT, int BM>
+struct TileGeom {
+  using C = FmtCfg<FMT>;
+  static constexpr int WM = BM >= 128 ? 2 : 1;
+  static constexpr int WN = 4 / WM;
+  static constexpr int TM = BM / WM / 32;
+  static constexpr int TN = GEMM_BN / WN / 32;
+  static constexpr int A_STAGE = BM * C::A_ROW;
+  static constexpr int B_STAGE = GEMM_BN * C::B_ROW;
+  static constexpr int A_SF_ROWS = BM < 64 ? 64 : BM;
+  static constexpr int A_SF_STAGE = C::SCALED ? A_SF_ROWS * 4 : 0;
+  static constexpr int B_SF_STAGE = C::SCALED ? (GEMM_BN / 32) * 128 : 0;
+  static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
+  static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // per wave
+  static constexpr int B_FRAGS_PER_NF = C::B_ROW * 32 / 1024;
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small");
+  static_assert(TN % 2 == 0, "gate/up pairs need an even number of N fragments");
+};
+
+template <int FMT, int BM, int LAYER>
+__global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
+  using C = FmtCfg<FMT>;
+  using G = TileGeom<FMT, BM>;
+  constexpr int TM = G::TM, TN = G::TN;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wm = w / G::WN, wn = w % G::WN;
+  const int NB = p.N / GEMM_BN;
+  const int nstages = p.K / C::KSTAGE;
+  const int total = p.meta[0] * NB;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
+
+  for (int base = 0; base < total; base += gridDim.x) {
+    const int u = base + xcd * per_xcd + xj;
+    if (u >= total) continue;
+    // ---- tile -> (expert, n block, m block)
+    int lo = 0, hi = p.num_experts - 1;
+    while (lo < hi) {  // largest e with tile_start(e) <= u
+      int mid = (lo + hi + 1) >> 1;
+      if ((p.offsets[mid] / BM) * NB <= u) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int mb0 = p.offsets[e] / BM;
+    const int mcount = p.offsets[e + 1] / BM - mb0;
+    const int local = u - mb0 * NB;
+    const int nb = local / mcount;
+    const int m0 = (mb0 + local % mcount) * BM;
+
+    // ---- per-lane A row offsets for the LDS-DMA copies
+    int64_t a_off[G::A_INSTR];
+#pragma unroll
+    for (int i = 0; i < G::A_INSTR; ++i) {
+      int r = (w * G::A_INSTR + i) * 8 + (lane >> 3);
+      int64_t row;
+      if (LAYER == 1) {
+        int s = p.sorted_slot[m0 + r];
+        row = s >= 0 ? s / p.kk : 0;
+      } else {
+        row = m0 + r;
+      }
+      a_off[i] = row * p.a_ld + ((lane & 7) ^ (lane >> 3)) * 16;
+    }
+    int64_t asf_off = 0;
+    const bool asf_wave = C::SCALED && (w * 64 < BM || (w == 0));
+    if constexpr (C::SCALED) {
+      int r = (w * 64 + lane) % BM;
+      int64_t row;
+      if (LAYER == 1) {
+        int s = p.sorted_slot[m0 + r];
+        row = s >= 0 ? s / p.kk : 0;
+      } else {
+        row = m0 + r;
+      }
+      asf_off = row * p.a_sf_ld;
+    }
+    const uint8_t* wexp = p.w + (int64_t)e * p.w_expert_bytes;
+    const uint8_t* wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
+
+    auto issue = [&](int s, int buf) {
+      uint8_t* st = smem + buf * G::STAGE;
+      // A rows
+#pragma unroll
+      for (int i = 0; i < G::A_INSTR; ++i)
+        g2lds16(p.a + a_off[i] + s * C::A_ROW, st + (w * G::A_INSTR + i) * 1024);
+      // weight fragments: [nf][stage][B_ROW * 32 bytes] per expert
+#pragma unroll
+      for (int i = 0; i < G::B_INSTR; ++i) {
+        int q = w * G::B_INSTR + i;
+        int nf = q / G::B_FRAGS_PER_NF, sub = q % G::B_FRAGS_PER_NF;
+        const uint8_t* src = wexp + ((int64_t)(nb * 8 + nf) * nstages + s) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
+        g2lds16(src, st + G::A_STAGE + q * 1024);
+      }
+      if constexpr (C::SCALED) {
+        // A scales: 4 UE8M0 bytes (this stage's 4 blocks) per row
+        if (asf_wave) {
+          __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
+                                           (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
+        }
+        // B scales: [nf][stage][64 lanes x 2 k-steps]
+        if (w == 0) {
+          const uint8_t* src = wsf + ((int64_t)(nb * 8 + (lane >> 3)) * nstages + s) * 128 + (lane & 7) * 16;
+          g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE);
+        }
+      }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    __syncthreads();   // the previous tile's readers are done with both buffers
+    issue(0, 0);
+    for (int s = 0; s < nstages; ++s) {
+      wait_vmcnt0();
+      __syncthreads();
+      if (s + 1 < nstages) issue(s + 1, (s + 1) & 1);
+      const uint8_t* st = smem + (s & 1) * G::STAGE;
+      const uint8_t* As = st;
+      const uint8_t* Bs = st + G::A_STAGE;
+      if constexpr (FMT == F_BF16) {
+#pragma unroll
+        for (int ks = 0; ks < C::STEPS; ++ks) {
+          bf16x8 af[TM], bfr[TN];
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) {
+            int r = wm * TM * 32 + tm * 32 + l32;
+            af[tm] = *(const bf16x8*)(As + r * 128 + (((ks * 2 + g) ^ (r & 7)) << 4));
+          }
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            bfr[tn] = *(const bf16x8*)(Bs + ((wn * TN + tn) * 4 + ks) * 1024 + lane * 16);
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+        }
+      } else {
+        const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
+        const uint8_t* Bsf = Asf + G::A_SF_STAGE;
+        uint32_t sa4[TM], sb2[TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) sa4[tm] = *(const uint32_t*)(Asf + (wm * TM * 32 + tm * 32 + l32) * 4);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) sb2[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
+#pragma unroll
+        for (int ks = 0; ks < C::STEPS; ++ks) {
+          i32x8 af[TM], bfr[TN];
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) {
+            int r = wm * TM * 32 + tm * 32 + l32;
+            i32x4 lo4 = *(const i32x4*)(As + r * 128 + (((ks * 4 + g) ^ (r & 7)) << 4));
+            i32x4 hi4 = *(const i32x4*)(As + r * 128 + (((ks * 4 + 2 + g) ^ (r & 7)) << 4));
+            af[tm] = (i32x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          }
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            int nf = wn * TN + tn;
+            if constexpr (FMT == F_MXFP8) {
+              const uint8_t* f = Bs + (nf * 2 + ks) * 2048 + lane * 16;
+              i32x4 lo4 = *(const i32x4*)f, hi4 = *(const i32x4*)(f + 1024);
+              bfr[tn] = (i32x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            } else {
+              i32x4 v4 = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
+              bfr[tn] = (i32x8){v4[0], v4[1], v4[2], v4[3], 0, 0, 0, 0};
+            }
+          }
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) {
+            int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+              int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[tm], bfr[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- epilogue.  Accumulator element v of lane l is row
+    // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32 of its 32x32 tile.
+    if constexpr (LAYER == 1) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int pp = 0; pp < TN / 2; ++pp) {
+          const int icol = nb * (GEMM_BN / 2) + (wn * (TN / 2) + pp) * 32 + l32;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+            float a = act_swiglu(acc[tm][2 * pp][v], acc[tm][2 * pp + 1][v], p);
+            if constexpr (FMT == F_BF16) {
+              ((uint16_t*)(p.c + (int64_t)row * p.c_ld))[icol] = bf16_rne(a);
+            } else {
+              // MXFP8 L2 input: one UE8M0 scale per 32 intermediate columns,
+              // which are exactly the 32 lanes of this half-wave.
+              float amax = group_max<5>(__builtin_fabsf(a));
+              uint32_t q = 0;
+              int c = 0;
+              if (amax > 0.0f) {
+                c = mx_scale_code<false>(amax);
+                q = e4m3_encode(__builtin_ldexpf(a, 127 - c));
+              }
+              p.c[(int64_t)row * p.c_ld + icol] = (uint8_t)q;
+              if (l32 == 0) p.c_sf[(int64_t)row * p.c_sf_ld + (icol >> 5)] = (uint8_t)c;
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          const int slot = p.sorted_slot[row];
+          if (slot < 0) continue;
+          float* orow = p.o + (int64_t)slot * p.N;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) orow[nb * GEMM_BN + (wn * TN + tn) * 32 + l32] = acc[tm][tn][v];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+template <int FMT, int BM, int LAYER>
+static hipError_t set_lds_attr() {
+  return hipFuncSetAttribute((const void*)k_gemm<FMT, BM, LAYER>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             TileGeom<FMT, BM>::LDS);
+}
+
+template <int FMT, int BM>
+static hipError_t init_fmt_bm() {
+  hipError_t e = set_lds_attr<FMT, BM, 1>();
+  if (e != hipSuccess) return e;
+  return set_lds_attr<FMT, BM, 2>();
+}
+
+template <int FMT>
+static hipError_t init_fmt() {
+  hipError_t e;
+  if ((e = init_fmt_bm<FMT, 32>()) != hipSuccess) return e;
+  if ((e = init_fmt_bm<FMT, 64>()) != hipSuccess) return e;
+  if ((e = init_fmt_bm<FMT, 128>()) != hipSuccess) return e;
+  return init_fmt_bm<FMT, 256>();
+}
+
+hipError_t gemm_init(int /*device*/) {
+  hipError_t e;
+  if ((e = init_fmt<F_BF16>()) != hipSuccess) return e;
+  if ((e = init_fmt<F_MXFP8>()) != hipSuccess) return e;
+  return init_fmt<F_MXFP4>();
+}
+
+template <int FMT, int BM>
+static hipError_t launch_fmt_bm(int layer, const GemmArgs& a, int grid, hipStream_t st) {
+  constexpr int lds = TileGeom<FMT, BM>::LDS;
+  if (layer == 1)
+    hipLaunchKernelGGL((k_gemm<FMT, BM, 1>), dim3(grid), dim3(GEMM_THREADS), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm<FMT, BM, 2>), dim3(grid), dim3(GEMM_THREADS), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_fmt(int layer, int bm, const GemmArgs& a, int grid, hipStream_t st) {
+  switch (bm) {
+    case 32: return launch_fmt_bm<FMT, 32>(layer, a, grid, st);
+    case 64: return launch_fmt_bm<FMT, 64>(layer, a, grid, st);
+    case 128: return launch_fmt_bm<FMT, 128>(layer, a, grid, st);
+    default: return launch_fmt_bm<FMT, 256>(layer, a, grid, st);
+  }
+}
+
+hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& a, int grid, hipStream_t st) {
+  switch (fmt) {
+    case F_BF16: return launch_fmt<F_BF16>(layer, bm, a, grid, st);
+    case F_MXFP8: return launch_fmt<F_MXFP8>(layer, bm, a, grid, st);
+    case F_MXFP4: return launch_fmt<F_MXFP4>(layer, bm, a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,77 @@
+// Host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_LOCAL_EXPERTS = 1000;  // E' = local + shared experts
+constexpr int GEMM_THREADS = 256;        // 4 waves per workgroup
+constexpr int GEMM_BN = 256;             // N columns per tile
+
+// Arguments of one grouped GEMM launch (L1 or L2).
+struct GemmArgs {
+  // A operand: rows of x (L1, gathered through sorted_slot / k') or of the
+  // L2 input (L2, already in sorted order).
+  const uint8_t* a;        // element codes (BF16 / E4M3 / packed E2M1)
+  const uint8_t* a_sf;     // block scales (UE8M0 or E4M3), NULL for BF16
+  const float* a_tok;      // NVFP4 L1: per-token global scale
+  int64_t a_ld;            // bytes per A row
+  int64_t a_sf_ld;         // bytes per A scale row
+  // B operand: kernel-layout weights of all local experts.
+  const uint8_t* w;
+  const uint8_t* w_sf;
+  const float* w_gs;       // NVFP4 per-expert global scale
+  int64_t w_expert_bytes;
+  int64_t w_sf_expert_bytes;
+  int N, K;                // GEMM N (2I for L1, H for L2) and K (H or I)
+  // routing
+  const int32_t* sorted_slot;
+  const int32_t* offsets;  // [E'+1], multiples of BLOCK_M
+  const int32_t* meta;     // meta[0] = number of BLOCK_M tiles
+  int num_experts;         // E'
+  int kk;                  // slots per token (top_k + shared)
+  // L1 epilogue: activation + L2-input quantisation into (c, c_sf)
+  uint8_t* c;
+  uint8_t* c_sf;
+  int64_t c_ld, c_sf_ld;
+  int inter;
+  int has_clamp;
+  float clamp, alpha, beta;
+  float l2_scale;          // NVFP4 global scale of the L2 input
+  // L2 epilogue: float32 rows per slot [S, H]
+  float* o;
+};
+
+enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
+
+void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+                     int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                     int32_t* tile_expert, int32_t* meta, hipStream_t stream);
+
+hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& args, int grid, hipStream_t stream);
+hipError_t gemm_init(int device);
+
+void launch_combine(const float* o, const int32_t* slot_row, const float* topk_w, int T, int k, int kk,
+                    int H, uint16_t* out, hipStream_t stream);
+
+void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13_sf,
+                      const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w13_k, uint8_t* w13_sf_k,
+                      uint8_t* w2_k, uint8_t* w2_sf_k, hipStream_t stream);
+
+// MX quantiser: rows x cols (cols % 32 == 0), BF16 or float32 source;
+// fp4 selects E2M1 elements (two per byte), else E4M3.
+void launch_quant_mx(bool fp4, bool f32, int64_t rows, int cols, const void* src, uint8_t* codes, uint8_t* scales,
+                     hipStream_t stream);
+
+// NVFP4 quantiser, one row per workgroup.  fixed_g != NULL: row r uses
+// fixed_g[r / rows_per_g]; else the row's own amax / (6 * 448) is used and
+// written to row_g[r].
+void launch_quant_nv(bool f32, int64_t rows, int cols, const void* src, uint8_t* codes, uint8_t* scales,
+                     float* row_g, const float* fixed_g, int rows_per_g, hipStream_t stream);
+
+void launch_weight_gscale(int E, int64_t per_expert, const float* src, float* gscale, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,163 @@
+// Block quantisers: dispatch quantisation of x and the weight casts.
+//
+// MX (DeepGEMM MegaMoE experts page, module docstring: one UE8M0 scale per
+// 1x32 block; Qwen4-Exp MegaMoE page, _requantize: power-of-two float32
+// scales whose exponent byte is the code): the scale is the smallest power of
+// two that keeps the block's largest magnitude within the element format, the
+// elements are value / scale rounded to nearest even.
+// NVFP4 (same module docstring: E4M3 scale per 1x16 block plus an FP32 global
+// scale; dispatch scales each token by its own FP32 scale): global g, block
+// scale bs = E4M3(amax16 / (6 g)), elements E2M1(v * (1 / (bs g))), all in
+// float32 arithmetic.  The token scale is amax_t / (6 * 448).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+template <bool F32>
+__device__ __forceinline__ float load_elem(const void* src, int64_t i) {
+  if (F32) return ((const float*)src)[i];
+  uint32_t b = (uint32_t)((const uint16_t*)src)[i] << 16;
+  return u2f(b);
+}
+
+// One thread per 32-element MX block.  Element codes are written unpacked
+// for E4M3 and two per byte for E2M1.
+template <bool F32, bool FP4>
+__global__ void __launch_bounds__(256) k_quant_mx(const void* __restrict__ src, int64_t nblocks,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+#pragma clang fp contract(off)
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = load_elem<F32>(src, b * 32 + i);
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  }
+  int c = 0;
+  uint32_t q[32];
+  if (amax > 0.0f) {
+    c = mx_scale_code<FP4>(amax);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float x = __builtin_ldexpf(v[i], 127 - c);
+      q[i] = FP4 ? e2m1_encode(x) : e4m3_encode(x);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) q[i] = 0;
+  }
+  scales[b] = (uint8_t)c;
+  if (FP4) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[j] |= q[j * 8 + i] << (4 * i);
+    }
+    *(uint4*)(codes + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      w[j] = q[4 * j] | (q[4 * j + 1] << 8) | (q[4 * j + 2] << 16) | (q[4 * j + 3] << 24);
+    *(uint4*)(codes + b * 32) = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(codes + b * 32 + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// NVFP4: one workgroup per row.  The row's global scale is either given
+// (fixed_g[row / rows_per_g]) or computed from the row's amax and written to
+// row_g[row].  Codes are packed two per byte.
+template <bool F32>
+__global__ void __launch_bounds__(256) k_quant_nv(const void* __restrict__ src, int cols,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  float* __restrict__ row_g, const float* __restrict__ fixed_g,
+                                                  int rows_per_g) {
+#pragma clang fp contract(off)
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t base = row * cols;
+  float g;
+  if (fixed_g) {
+    g = fixed_g[row / rows_per_g];
+  } else {
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < cols; i += 256) amax = __builtin_fmaxf(amax, __builtin_fabsf(load_elem<F32>(src, base + i)));
+    amax = group_max<6>(amax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    g = amax > 0.0f ? amax / 2688.0f : 1.0f;
+    if (threadIdx.x == 0) row_g[row] = g;
+  }
+  const float six_g = 6.0f * g;
+  for (int blk = threadIdx.x; blk < cols / 16; blk += 256) {
+    float v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = load_elem<F32>(src, base + blk * 16 + i);
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    }
+    const float t = amax / six_g;
+    const uint32_t bs = e4m3_encode(t);
+    const float bsv = e4m3_decode(bs);
+    uint32_t w[2] = {0, 0};
+    if (bsv != 0.0f) {
+      const float r = 1.0f / (bsv * g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_encode(v[i] * r) << (4 * (i & 7));
+    }
+    scales[row * (cols / 16) + blk] = (uint8_t)bs;
+    *(uint2*)(codes + (base + blk * 16) / 2) = make_uint2(w[0], w[1]);
+  }
+}
+
+// Per-expert amax -> NVFP4 global scale amax / (6 * 448) (1 if zero).
+__global__ void __launch_bounds__(256) k_weight_gscale(const float* __restrict__ src, int64_t per_expert,
+                                                       float* __restrict__ gscale) {
+  __shared__ float red[4];
+  const float* p = src + (int64_t)blockIdx.x * per_expert;
+  float amax = 0.0f;
+  for (int64_t i = threadIdx.x; i < per_expert; i += 256) amax = __builtin_fmaxf(amax, __builtin_fabsf(p[i]));
+  amax = group_max<6>(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    gscale[blockIdx.x] = m > 0.0f ? m / 2688.0f : 1.0f;
+  }
+}
+
+void launch_weight_gscale(int E, int64_t per_expert, const float* src, float* gscale, hipStream_t st) {
+  hipLaunchKernelGGL(k_weight_gscale, dim3(E), dim3(256), 0, st, src, per_expert, gscale);
+}
+
+void launch_quant_mx(bool fp4, bool f32, int64_t rows, int cols, const void* src, uint8_t* codes, uint8_t* scales,
+                     hipStream_t st) {
+  const int64_t nblocks = rows * (cols / 32);
+  const dim3 grid((unsigned)((nblocks + 255) / 256));
+  if (f32) {
+    if (fp4) hipLaunchKernelGGL((k_quant_mx<true, true>), grid, dim3(256), 0, st, src, nblocks, codes, scales);
+    else hipLaunchKernelGGL((k_quant_mx<true, false>), grid, dim3(256), 0, st, src, nblocks, codes, scales);
+  } else {
+    if (fp4) hipLaunchKernelGGL((k_quant_mx<false, true>), grid, dim3(256), 0, st, src, nblocks, codes, scales);
+    else hipLaunchKernelGGL((k_quant_mx<false, false>), grid, dim3(256), 0, st, src, nblocks, codes, scales);
+  }
+}
+
+void launch_quant_nv(bool f32, int64_t rows, int cols, const void* src, uint8_t* codes, uint8_t* scales,
+                     float* row_g, const float* fixed_g, int rows_per_g, hipStream_t st) {
+  if (f32)
+    hipLaunchKernelGGL((k_quant_nv<true>), dim3((unsigned)rows), dim3(256), 0, st, src, cols, codes, scales, row_g,
+                       fixed_g, rows_per_g);
+  else
+    hipLaunchKernelGGL((k_quant_nv<false>), dim3((unsigned)rows), dim3(256), 0, st, src, cols, codes, scales, row_g,
+                       fixed_g, rows_per_g);
+}
+
+}  // namespace moe

@@ -1,0 +1,126 @@
+"""The C-ABI library loads and exports every symbol include/moe.h declares;
+host-only entry points and argument validation work without a GPU (every
+validation failure returns before anything touches a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_gemms_amd as moe
+from expert_gemms_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(_lib.LIB_PATH), "build the library first (python -m expert_gemms_amd.build)"
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = moe.lib_handle()
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.moe_status_string(s), bytes)
+    assert lib.moe_status_string(-3) == b"workspace too small"
+
+
+def test_block_m_rule():
+    assert moe.moe_get_block_m(4096, 8, 0, 2, "bf16") == 256      # 1024 rows per expert
+    assert moe.moe_get_block_m(1, 128, 0, 8, "mxfp4") == 32
+    assert moe.moe_get_block_m(256, 128, 0, 8, "mxfp4") == 32      # 16 rows per expert
+    assert moe.moe_get_block_m(1000, 64, 0, 6, "nvfp4") == 128     # 93.75
+    assert moe.moe_get_block_m(0, 8, 0, 2, "bf16") == 32
+    with pytest.raises(moe.MoEError):
+        moe.moe_get_block_m(-1, 8, 0, 2, "bf16")
+    with pytest.raises(moe.MoEError):
+        moe.moe_get_block_m(8, 0, 0, 2, "bf16")
+
+
+def test_workspace_bytes():
+    b256 = moe.moe_workspace_bytes("bf16", 4096, 4096, 14336, 8, 0, 2, 256)
+    b32 = moe.moe_workspace_bytes("bf16", 4096, 4096, 14336, 8, 0, 2, 32)
+    assert b256 == moe.moe_workspace_bytes("bf16", 4096, 4096, 14336, 8, 0, 2, 0)
+    assert b256 > b32 > 8192 * 4096 * 4          # at least the float32 L2 rows
+    assert moe.moe_workspace_bytes("bf16", 4096, 4000, 14336, 8, 0, 2, 0) == 0   # H % 128
+    assert moe.moe_workspace_bytes("bf16", 4096, 4096, 14336, 8, 0, 2, 48) == 0  # bad block_m
+    assert moe.moe_workspace_bytes("mxfp8", 10, 7168, 2048, 256, 1, 8, 0) > 0
+
+
+class _Fake:
+    """Stands in for a tensor: an aligned, never-dereferenced address."""
+    def __init__(self, addr=0x10000, n=1 << 20):
+        self.addr, self.n = addr, n
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def _fwd(**kw):
+    lib = moe.lib_handle()
+    a = dict(fmt=0, T=4, H=256, I=256, k=2, start=0, nloc=4, nsh=0, bm=0, act=None,
+             x=_Fake(), ids=_Fake(), wts=_Fake(), w13=_Fake(), w13sf=None, w2=_Fake(), w2sf=None,
+             g13=None, g2=None, l2=1.0, out=_Fake(), ws=_Fake(), wsb=1 << 40)
+    a.update(kw)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    act = ctypes.byref(a["act"]) if a["act"] is not None else None
+    return lib.moe_forward(a["fmt"], a["T"], a["H"], a["I"], a["k"], a["start"], a["nloc"], a["nsh"], a["bm"],
+                           act, p(a["x"]), p(a["ids"]), p(a["wts"]), p(a["w13"]), p(a["w13sf"]), p(a["w2"]),
+                           p(a["w2sf"]), p(a["g13"]), p(a["g2"]), a["l2"], p(a["out"]), p(a["ws"]),
+                           a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=200), dict(I=100), dict(k=0), dict(nloc=0), dict(nsh=-1), dict(bm=48), dict(fmt=9),
+    dict(T=-1), dict(x=None), dict(out=None), dict(ws=None), dict(x=_Fake(0x10004)),
+    dict(fmt=1),                                 # MX without scale pointers
+    dict(fmt=3, w13sf=_Fake(), w2sf=_Fake()),    # NVFP4 without global scales
+    dict(fmt=3, w13sf=_Fake(), w2sf=_Fake(), g13=_Fake(), g2=_Fake(), l2=0.0),
+    dict(act=_lib.Activation(0, 0, 0.0, float("inf"), 0.0)),
+    dict(act=_lib.Activation(0, 1, -1.0, 1.0, 0.0)),
+    dict(nloc=999, nsh=2),                       # more than 1000 local experts
+])
+def test_forward_rejects_invalid_arguments(kw):
+    assert _fwd(**kw) == _lib.E_INVALID
+
+
+def test_forward_other_statuses_without_gpu():
+    assert _fwd(T=0) == _lib.OK                                  # nothing to do, nothing enqueued
+    assert _fwd(act=_lib.Activation(1, 0, 0.0, 1.0, 0.0)) == _lib.E_UNSUPPORTED
+    assert _fwd(wsb=16) == _lib.E_WORKSPACE
+    # all arguments valid: the device check fails cleanly on a GPU-less host
+    import torch
+    if not torch.cuda.is_available():
+        assert _fwd() == _lib.E_UNSUPPORTED
+
+
+def test_other_entry_points_validate():
+    lib = moe.lib_handle()
+    P = ctypes.c_void_p
+    f = P(0x10000)
+    assert lib.moe_dispatch(4, 2, 0, 0, 4, 48, f, f, f, f, f, f, None) == _lib.E_INVALID
+    assert lib.moe_dispatch(4, 0, 0, 0, 4, 32, f, f, f, f, f, f, None) == _lib.E_INVALID
+    assert lib.moe_quantize_x(0, 4, 256, f, f, f, None, None) == _lib.E_INVALID       # BF16 has no quantiser
+    assert lib.moe_quantize_x(1, 4, 100, f, f, f, None, None) == _lib.E_INVALID
+    assert lib.moe_quantize_x(3, 4, 256, f, f, f, None, None) == _lib.E_INVALID       # NVFP4 needs token scales
+    assert lib.moe_quantize_weights(1, 2, 64, 48, f, f, f, None, None) == _lib.E_INVALID
+    assert lib.moe_transform_weights(0, 2, 200, 256, f, None, f, None, f, None, f, None, None) == _lib.E_INVALID
+    assert lib.moe_transform_weights(1, 2, 256, 256, f, None, f, None, f, None, f, None, None) == _lib.E_INVALID

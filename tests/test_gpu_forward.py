@@ -1,0 +1,98 @@
+"""moe_forward (the whole HIP path: a1-a7) against the oracle, element by
+element, on seeded inputs that span several tiles and ragged tails.
+
+Bar (tests/helpers.check_output): |y_gpu - y_oracle| <= tol * RMS(y_oracle)
++ half a BF16 ulp of y_oracle, tol = 1e-2 for BF16 and 3e-2 for MX/NVFP4.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.moe import moe_reference
+from synth import CONFIGS, MoEConfig, gen_routing, gen_x_bf16, bf16_bits
+from tests.gpu_util import run_layer
+from tests.helpers import check_output, make_weights
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_bf16": CONFIGS["tiny_bf16"],
+    "bf16_small": MoEConfig("bf16_small", 11, "bf16", 200, 512, 384, 8, 2, routing="softmax_uniform"),
+    "mxfp8_small": MoEConfig("mxfp8_small", 12, "mxfp8", 150, 512, 256, 16, 4, num_shared=1,
+                             routing="sigmoid_normal"),
+    "mxfp4_small": MoEConfig("mxfp4_small", 13, "mxfp4", 37, 512, 384, 32, 8, routing="softmax_uniform"),
+}
+
+_CACHE = {}
+
+
+def inputs(cfg):
+    if cfg.name not in _CACHE:
+        x = bf16_bits(gen_x_bf16(cfg))
+        ids, wts = gen_routing(cfg)
+        if cfg.num_shared:
+            pass
+        _CACHE[cfg.name] = (x, ids, wts, make_weights(cfg))
+    return _CACHE[cfg.name]
+
+
+def compare(cfg, block_m=0, act=None, **kw):
+    x, ids, wts, w = inputs(cfg)
+    y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=block_m, act=act, **kw)
+    ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, act=act)
+    rel, excess = check_output(cfg.fmt, y, ref)
+    print(f"{cfg.name} bm={block_m}: max|err|/RMS = {rel:.3e}")
+    assert excess <= 0, (rel, excess)
+    return y
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_forward_matches_oracle(name):
+    compare(SMALL[name])
+
+
+@pytest.mark.parametrize("bm", [32, 64, 128, 256])
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small"])
+def test_forward_every_block_m(name, bm):
+    compare(SMALL[name], block_m=bm)
+
+
+def test_forward_activation_variants():
+    cfg = SMALL["bf16_small"]
+    compare(cfg, act={"clamp": 0.75, "alpha": 1.702, "beta": 1.0})
+    compare(cfg, act={"clamp": None, "alpha": 0.5, "beta": -0.25})
+
+
+def test_forward_expert_range_and_dropped_slots():
+    """A GPU holding experts 2..5 of 8: other ids (and -1) drop their slots."""
+    cfg = SMALL["bf16_small"]
+    x, ids, wts, w = inputs(cfg)
+    ids = ids.copy()
+    ids[::7, 1] = -1
+    w_loc = {k: v[2:6] for k, v in w.items()}
+    y, _ = run_layer("bf16", x, ids, wts, w_loc, expert_start=2, num_local=4)
+    ref = moe_reference("bf16", x, ids, wts, w_loc, expert_start=2, num_local=4)
+    rel, excess = check_output("bf16", y, ref)
+    assert excess <= 0, rel
+    none_local = ~np.isin(ids, [2, 3, 4, 5]).any(axis=1)
+    assert none_local.any() and not y[none_local].any()      # such tokens get zeros
+
+
+def test_forward_all_dropped_and_single_token():
+    cfg = SMALL["mxfp8_small"]
+    x, ids, wts, w = inputs(cfg)
+    w_r = {k: v[:cfg.E] for k, v in w.items()}
+    y, _ = run_layer("mxfp8", x, np.full_like(ids, -1), wts, w_r)
+    assert not y.any()
+    y1, _ = run_layer("mxfp8", x[:1], ids[:1], wts[:1], w_r)
+    ref1 = moe_reference("mxfp8", x[:1], ids[:1], wts[:1], w_r)
+    assert check_output("mxfp8", y1, ref1)[1] <= 0
+
+
+def test_forward_deterministic():
+    cfg = SMALL["mxfp8_small"]
+    x, ids, wts, w = inputs(cfg)
+    a, layer = run_layer("mxfp8", x, ids, wts, w, num_shared=1)
+    b, _ = run_layer("mxfp8", x, ids, wts, w, num_shared=1)
+    assert np.array_equal(a, b)
