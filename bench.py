@@ -1,0 +1,266 @@
+"""Benchmark of the fused MoE routed-expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--tokens T]
+                    [--flush-mb MB] [--no-cpu-baseline]
+
+A step is one moe_forward call (dispatch quantisation, routing metadata, L1
+GEMM + SwiGLU + L2-input quantisation, L2 GEMM, weighted combine) over one
+batch of synthetic input already resident in HBM.  W untimed warm-up steps,
+then exactly K steps between two synchronisations; one JSON line on stdout.
+
+Default workload: the Mixtral-8x7B-shaped BF16 layer (4096 tokens, hidden
+4096, intermediate 14336, 8 experts, top-2).  --config picks another seeded
+workload (tiny_bf16, mixtral_bf16, dsv3_mxfp8, decode_mxfp4, nvfp4_zipf).
+
+Roofline: the dominant kernel is timed live with HIP events recorded by the
+library on the stream it launches on (moe_forward_profiled).  Its algorithmic
+work is 4 * S * H * I FLOPs for the L1 GEMM (S real slots; padding rows are
+overhead) or the weight bytes it must stream, against MI355X's published
+peaks (dense MFMA BF16 2500 TFLOP/s, FP8 5000; HBM 8000 GB/s).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 5000.0, "nvfp4": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="mixtral_bf16")
+    p.add_argument("--tokens", type=int, default=None, help="token count (decode workload)")
+    p.add_argument("--flush-mb", type=int, default=0, help="write this many MB between steps (defeats the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="only run a plain device copy of this many MB (HBM counter calibration)")
+    return p.parse_args()
+
+
+def copy_calibration(mb, reps=3):
+    """A plain device-to-device copy of known size: FETCH_SIZE / WRITE_SIZE of
+    this kernel calibrate the HBM byte counters (reads mb MB, writes mb MB)."""
+    src = torch.ones(mb * (1 << 20), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mb": mb, "reps": reps, "bytes_read_per_copy": mb * (1 << 20),
+                      "bytes_written_per_copy": mb * (1 << 20)}), flush=True)
+    return 0
+
+
+def elem_bytes(fmt):
+    return {"bf16": 2.0, "mxfp8": 1.0, "mxfp4": 0.5, "nvfp4": 0.5}[fmt]
+
+
+def scale_bytes_per_elem(fmt):
+    return {"bf16": 0.0, "mxfp8": 1 / 32, "mxfp4": 1 / 32, "nvfp4": 1 / 16}[fmt]
+
+
+def build_layer(cfg, T, device):
+    """Seeded inputs on the device, weights quantised by the library's own
+    quantiser and transformed to the kernel layout."""
+    import expert_gemms_amd as moe
+    from synth import gen_x_bf16, gen_routing, gen_weight_f32_device, gen_w2_input_scale
+
+    fmt = cfg.fmt
+    E = cfg.E + cfg.num_shared
+    H, I = cfg.H, cfg.I
+    x = gen_x_bf16(cfg, T).to(device)
+    ids, wts = gen_routing(cfg, T)
+    ids_d = torch.from_numpy(ids).to(device)
+    wts_d = torch.from_numpy(wts).to(device)
+    vpe = 2 if fmt in ("mxfp4", "nvfp4") else 1
+    grp = 16 if fmt == "nvfp4" else 32
+    canon = {}
+    for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+        if fmt == "bf16":
+            w = torch.empty((E, N, K), dtype=torch.bfloat16, device=device)
+            for e in range(E):
+                w[e].copy_(gen_weight_f32_device(cfg, name, e, device))
+            canon[name] = w
+        else:
+            codes = torch.empty((E, N, K // vpe), dtype=torch.uint8, device=device)
+            sf = torch.empty((E, N, K // grp), dtype=torch.uint8, device=device)
+            gs = torch.empty((E,), dtype=torch.float32, device=device) if fmt == "nvfp4" else None
+            for e in range(E):
+                src = gen_weight_f32_device(cfg, name, e, device)
+                moe.moe_quantize_weights(fmt, 1, N, K, src, codes[e], sf[e],
+                                         gs[e:e + 1] if gs is not None else None)
+                del src
+            canon[name], canon[name + "_sf"] = codes, sf
+            if gs is not None:
+                canon[name + "_gs"] = gs
+    layer = moe.FusedMoE(fmt, H, I, cfg.E, cfg.top_k, num_shared=cfg.num_shared, max_tokens=T)
+    w2_in = torch.from_numpy(gen_w2_input_scale(cfg)) if fmt == "nvfp4" else None
+    layer.load_canonical(canon["w13"], canon["w2"], canon.get("w13_sf"), canon.get("w2_sf"),
+                         canon.get("w13_gs"), canon.get("w2_gs"), w2_input_scale=w2_in)
+    torch.cuda.synchronize()
+    return layer, x, ids, wts, ids_d, wts_d, canon
+
+
+def algorithmic(cfg, T, ids):
+    """FLOPs and bytes the method itself must compute and move."""
+    S = T * (cfg.top_k + cfg.num_shared)
+    flops = 6.0 * S * cfg.H * cfg.I
+    touched = np.unique(ids[(ids >= 0) & (ids < cfg.E)]).size + cfg.num_shared
+    per_expert_elems = 3.0 * cfg.H * cfg.I
+    wbytes = touched * per_expert_elems * (elem_bytes(cfg.fmt) + scale_bytes_per_elem(cfg.fmt))
+    if cfg.fmt == "nvfp4":
+        wbytes += touched * 8
+    io = T * cfg.H * 2 * 2 + T * cfg.top_k * 8
+    l1_flops = 4.0 * S * cfg.H * cfg.I
+    l1_wbytes = touched * 2.0 * cfg.H * cfg.I * (elem_bytes(cfg.fmt) + scale_bytes_per_elem(cfg.fmt))
+    return flops, wbytes + io, l1_flops, l1_wbytes, touched
+
+
+def cpu_baseline(cfg, T, x, ids, wts, canon, n_tok):
+    """The oracle as it stands, on the host cores, over the first n_tok tokens."""
+    from oracle.moe import moe_reference
+    from synth import bf16_bits
+    from threadpoolctl import threadpool_info
+
+    w = {}
+    for k, v in canon.items():
+        a = v.cpu().contiguous()
+        w[k] = a.view(torch.int16).numpy().view(np.uint16) if a.dtype == torch.bfloat16 else a.numpy()
+    xb = bf16_bits(x[:n_tok])
+    l2 = 1.0
+    if cfg.fmt == "nvfp4":
+        from synth import gen_w2_input_scale
+        m = float(gen_w2_input_scale(cfg).max())
+        l2 = m if m > 0 else 1.0
+    t0 = time.perf_counter()
+    moe_reference(cfg.fmt, xb, ids[:n_tok], wts[:n_tok], w, num_shared=cfg.num_shared,
+                  l2_activation_scale=l2)
+    dt = time.perf_counter() - t0
+    S = n_tok * (cfg.top_k + cfg.num_shared)
+    flops = 6.0 * S * cfg.H * cfg.I
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tok} of {T} tokens of the same workload ({S} slots, all touched experts "
+                      f"dequantised); {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer's expert-parallel path across GPUs is not built)", file=sys.stderr)
+        return 2
+    if args.copy_mb:
+        return copy_calibration(args.copy_mb)
+    from synth import CONFIGS
+    import expert_gemms_amd as moe
+
+    cfg = CONFIGS[args.config]
+    T = args.tokens if args.tokens is not None else cfg.T
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    layer, x, ids, wts, ids_d, wts_d, canon = build_layer(cfg, T, device)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(args.flush_mb * (1 << 20), dtype=torch.uint8, device=device) if args.flush_mb else None
+
+    nsteps = len(moe._lib.STEPS)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nsteps)]
+        for e in evs:
+            e.record(stream)          # creates the underlying hipEvent
+        return evs
+
+    for _ in range(args.warmup):
+        layer.forward(x, ids_d, wts_d, out=out)
+    torch.cuda.synchronize()
+
+    step_events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        layer.forward(x, ids_d, wts_d, out=out, step_events=step_events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    per_step = {name: float(np.mean([ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in step_events]))
+                for j, name in enumerate(moe._lib.STEPS)}
+    step_ms = [ev[0].elapsed_time(ev[2 * nsteps - 1]) for ev in step_events]
+    ms_per_step = float(np.mean(step_ms)) if flush is not None else t_start.elapsed_time(t_end) / args.steps
+
+    flops, hbm_bytes, l1_flops, l1_wbytes, touched = algorithmic(cfg, T, ids)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    gbs = hbm_bytes / (ms_per_step * 1e-3) / 1e9
+    l1_ms = per_step["l1"]
+    peak = PEAK_TFLOPS[cfg.fmt]
+    prefill = l1_flops / l1_wbytes > peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if prefill:
+        achieved = l1_flops / (l1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": "L1 grouped GEMM"}
+    else:
+        achieved = l1_wbytes / (l1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "L1 grouped GEMM"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or min(T, 1024)
+        cpu = cpu_baseline(cfg, T, x, ids, wts, canon, n_tok)
+
+    S = T * (cfg.top_k + cfg.num_shared)
+    rec = {
+        "metric": "MoE-layer TFLOP/s (HBM GB/s alongside; fraction of MI355X peak) per format",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.fmt,
+        "data": "synthetic (seeded; random-init weights of the named shape)",
+        "config": {"workload": cfg.name, "format": cfg.fmt, "tokens": T, "hidden": cfg.H, "inter": cfg.I,
+                   "experts": cfg.E, "shared": cfg.num_shared, "top_k": cfg.top_k, "slots": S,
+                   "touched_experts": int(touched), "block_m": layer_block_m(cfg, T),
+                   "flush_mb": args.flush_mb},
+        "hbm_gbps": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "mfma_frac": round(tflops / peak, 4),
+        "step_ms": {k: round(v, 4) for k, v in per_step.items()},
+        "wall_s": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def layer_block_m(cfg, T):
+    import expert_gemms_amd as moe
+    return moe.moe_get_block_m(T, cfg.E, cfg.num_shared, cfg.top_k, cfg.fmt)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

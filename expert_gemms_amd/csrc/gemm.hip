@@ -23,8 +23,9 @@
 // fragments and block scales are copied global -> LDS by the LDS-DMA path
 // (global_load_lds_dwordx4) into one of two buffers while the MFMAs consume
 // the other.  A rows sit in LDS as 128-byte rows whose 16-byte chunks are
-// XOR-swizzled by (row & 7), so the 8 lanes a ds_read_b128 services at once
-// hit 8 distinct bank groups.  Weights arrive in the kernel layout written by
+// XOR-swizzled (see swz) so each ds_read_b128 phase is bank-conflict free.
+// Fragments of K-step ks+1 are read into a second register set while the
+// MFMAs of K-step ks run.  Weights arrive in the kernel layout written by
 // moe_transform_weights: each 32-row x K-step fragment is 1 KiB (or 2 KiB)
 // in register order, so the weight copy and its LDS reads are linear.
 #include "common.h"
@@ -76,11 +77,89 @@ struct TileGeom {
   static_assert(TN % 2 == 0, "gate/up pairs need an even number of N fragments");
 };
 
+// LDS A rows are 128 bytes (8 chunks of 16 bytes).  gfx950 LDS serves 16
+// lanes x 16 bytes per cycle from 64 banks, so the 16 rows a ds_read_b128
+// phase touches must land on 16 distinct 16-byte bank groups: rows r and r+1
+// already differ by 128 bytes, so the chunk index is XORed with (r >> 1) & 7.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// MFMA operand fragments of one K-step.
+template <int FMT> struct Frag;
+template <> struct Frag<F_BF16> { using A = bf16x8; using B = bf16x8; };
+template <> struct Frag<F_MXFP8> { using A = i32x8; using B = i32x8; };
+template <> struct Frag<F_MXFP4> { using A = i32x8; using B = i32x8; };
+
+template <int FMT, int TM, int TN>
+__device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int ks, int wm, int wn, int lane,
+                                           typename Frag<FMT>::A (&af)[TM], typename Frag<FMT>::B (&bf)[TN]) {
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int r = wm * TM * 32 + tm * 32 + l32;
+    if constexpr (FMT == F_BF16) {
+      af[tm] = *(const bf16x8*)(As + r * 128 + (swz(r, ks * 2 + g) << 4));
+    } else {
+      // 8-bit A operand: register bytes 0-15 hold K [16g, 16g+16) of the
+      // 64-wide K-step, bytes 16-31 hold K [32+16g, +16)
+      const i32x4 lo = *(const i32x4*)(As + r * 128 + (swz(r, ks * 4 + g) << 4));
+      const i32x4 hi = *(const i32x4*)(As + r * 128 + (swz(r, ks * 4 + 2 + g) << 4));
+      af[tm] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int nf = wn * TN + tn;
+    if constexpr (FMT == F_BF16) {
+      bf[tn] = *(const bf16x8*)(Bs + (nf * 4 + ks) * 1024 + lane * 16);
+    } else if constexpr (FMT == F_MXFP8) {
+      const uint8_t* f = Bs + (nf * 2 + ks) * 2048 + lane * 16;
+      const i32x4 lo = *(const i32x4*)f, hi = *(const i32x4*)(f + 1024);
+      bf[tn] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const i32x4 v = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
+      bf[tn] = (i32x8){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    }
+  }
+}
+
+// Scheduling hint for one K stage, as an ordered list of instruction groups:
+// the first K-step's LDS reads (FIRST), then MFMA by MFMA: after MFMA j of
+// K-step ks (ks < STEPS - 1) its share of the next step's READS reads, and,
+// over the first half of the stage, its share of the VMEM global->LDS copies
+// for the next stage, so no wave stalls issuing a burst of copies.
+template <int J, int STEPS, int READS, int MFMAS, int VMEM>
+__device__ __forceinline__ void stage_mfma_hint() {
+  constexpr int TOTAL = STEPS * MFMAS;
+  if constexpr (J < TOTAL) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int ks = J / MFMAS, i = J % MFMAS;
+    if constexpr (ks + 1 < STEPS) {
+      constexpr int r = ((i + 1) * READS) / MFMAS - (i * READS) / MFMAS;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    }
+    constexpr int HALF = TOTAL / 2 > 0 ? TOTAL / 2 : 1;
+    if constexpr (J < HALF) {
+      constexpr int v = ((J + 1) * VMEM) / HALF - (J * VMEM) / HALF;
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    }
+    stage_mfma_hint<J + 1, STEPS, READS, MFMAS, VMEM>();
+  }
+}
+
+template <int STEPS, int FIRST, int READS, int MFMAS, int VMEM>
+__device__ __forceinline__ void stage_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+  stage_mfma_hint<0, STEPS, READS, MFMAS, VMEM>();
+}
+
 template <int FMT, int BM, int LAYER>
-__global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
+__global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_gemm(const GemmArgs p) {
   using C = FmtCfg<FMT>;
   using G = TileGeom<FMT, BM>;
+  using FA = typename Frag<FMT>::A;
+  using FB = typename Frag<FMT>::B;
   constexpr int TM = G::TM, TN = G::TN;
+  constexpr int READS = TM * (FMT == F_BF16 ? 1 : 2) + TN * (FMT == F_MXFP8 ? 2 : 1);
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -107,27 +186,28 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
     const int nb = local / mcount;
     const int m0 = (mb0 + local % mcount) * BM;
 
-    // ---- per-lane A row offsets for the LDS-DMA copies
+    // ---- per-lane A row offsets for the LDS-DMA copies: lane l of copy i
+    // fills LDS row r = 8 * (copy index) + l / 8, physical chunk l % 8
     int64_t a_off[G::A_INSTR];
 #pragma unroll
     for (int i = 0; i < G::A_INSTR; ++i) {
-      int r = (w * G::A_INSTR + i) * 8 + (lane >> 3);
+      const int r = (w * G::A_INSTR + i) * 8 + (lane >> 3);
       int64_t row;
       if (LAYER == 1) {
-        int s = p.sorted_slot[m0 + r];
+        const int s = p.sorted_slot[m0 + r];
         row = s >= 0 ? s / p.kk : 0;
       } else {
         row = m0 + r;
       }
-      a_off[i] = row * p.a_ld + ((lane & 7) ^ (lane >> 3)) * 16;
+      a_off[i] = row * p.a_ld + (swz(r, lane & 7) << 4);
     }
     int64_t asf_off = 0;
-    const bool asf_wave = C::SCALED && (w * 64 < BM || (w == 0));
+    const bool asf_wave = C::SCALED && (w * 64 < BM || w == 0);
     if constexpr (C::SCALED) {
-      int r = (w * 64 + lane) % BM;
+      const int r = (w * 64 + lane) % BM;
       int64_t row;
       if (LAYER == 1) {
-        int s = p.sorted_slot[m0 + r];
+        const int s = p.sorted_slot[m0 + r];
         row = s >= 0 ? s / p.kk : 0;
       } else {
         row = m0 + r;
@@ -139,25 +219,23 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
 
     auto issue = [&](int s, int buf) {
       uint8_t* st = smem + buf * G::STAGE;
-      // A rows
 #pragma unroll
       for (int i = 0; i < G::A_INSTR; ++i)
         g2lds16(p.a + a_off[i] + s * C::A_ROW, st + (w * G::A_INSTR + i) * 1024);
-      // weight fragments: [nf][stage][B_ROW * 32 bytes] per expert
+      // weight fragments: [32-row block][stage][B_ROW * 32 bytes] per expert
 #pragma unroll
       for (int i = 0; i < G::B_INSTR; ++i) {
-        int q = w * G::B_INSTR + i;
-        int nf = q / G::B_FRAGS_PER_NF, sub = q % G::B_FRAGS_PER_NF;
+        const int q = w * G::B_INSTR + i;
+        const int nf = q / G::B_FRAGS_PER_NF, sub = q % G::B_FRAGS_PER_NF;
         const uint8_t* src = wexp + ((int64_t)(nb * 8 + nf) * nstages + s) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
         g2lds16(src, st + G::A_STAGE + q * 1024);
       }
       if constexpr (C::SCALED) {
-        // A scales: 4 UE8M0 bytes (this stage's 4 blocks) per row
-        if (asf_wave) {
+        // A scales: this stage's 4 UE8M0 bytes of every row
+        if (asf_wave)
           __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
                                            (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
-        }
-        // B scales: [nf][stage][64 lanes x 2 k-steps]
+        // B scales: [32-row block][stage][64 lanes x 2 K-steps]
         if (w == 0) {
           const uint8_t* src = wsf + ((int64_t)(nb * 8 + (lane >> 3)) * nstages + s) * 128 + (lane & 7) * 16;
           g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE);
@@ -173,75 +251,52 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    __syncthreads();   // the previous tile's readers are done with both buffers
+    // the previous tile's copies have landed and its readers are done with
+    // both buffers
+    wait_vmcnt0();
+    __syncthreads();
     issue(0, 0);
     for (int s = 0; s < nstages; ++s) {
       wait_vmcnt0();
       __syncthreads();
-      if (s + 1 < nstages) issue(s + 1, (s + 1) & 1);
+      // unconditional, so the copies share a scheduling region with the
+      // MFMAs; the last stage re-copies itself into the idle buffer
+      issue(s + 1 < nstages ? s + 1 : s, (s + 1) & 1);
       const uint8_t* st = smem + (s & 1) * G::STAGE;
       const uint8_t* As = st;
       const uint8_t* Bs = st + G::A_STAGE;
-      if constexpr (FMT == F_BF16) {
-#pragma unroll
-        for (int ks = 0; ks < C::STEPS; ++ks) {
-          bf16x8 af[TM], bfr[TN];
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            int r = wm * TM * 32 + tm * 32 + l32;
-            af[tm] = *(const bf16x8*)(As + r * 128 + (((ks * 2 + g) ^ (r & 7)) << 4));
-          }
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn)
-            bfr[tn] = *(const bf16x8*)(Bs + ((wn * TN + tn) * 4 + ks) * 1024 + lane * 16);
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-        }
-      } else {
+      uint32_t sa4[TM], sb2[TN];
+      if constexpr (C::SCALED) {
         const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
         const uint8_t* Bsf = Asf + G::A_SF_STAGE;
-        uint32_t sa4[TM], sb2[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) sa4[tm] = *(const uint32_t*)(Asf + (wm * TM * 32 + tm * 32 + l32) * 4);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) sb2[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
+      }
+      FA af[2][TM];
+      FB bfr[2][TN];
+      load_frags<FMT, TM, TN>(As, Bs, 0, wm, wn, lane, af[0], bfr[0]);
 #pragma unroll
-        for (int ks = 0; ks < C::STEPS; ++ks) {
-          i32x8 af[TM], bfr[TN];
+      for (int ks = 0; ks < C::STEPS; ++ks) {
+        if (ks + 1 < C::STEPS) load_frags<FMT, TM, TN>(As, Bs, ks + 1, wm, wn, lane, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            int r = wm * TM * 32 + tm * 32 + l32;
-            i32x4 lo4 = *(const i32x4*)(As + r * 128 + (((ks * 4 + g) ^ (r & 7)) << 4));
-            i32x4 hi4 = *(const i32x4*)(As + r * 128 + (((ks * 4 + 2 + g) ^ (r & 7)) << 4));
-            af[tm] = (i32x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          }
+        for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
-            int nf = wn * TN + tn;
-            if constexpr (FMT == F_MXFP8) {
-              const uint8_t* f = Bs + (nf * 2 + ks) * 2048 + lane * 16;
-              i32x4 lo4 = *(const i32x4*)f, hi4 = *(const i32x4*)(f + 1024);
-              bfr[tn] = (i32x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            if constexpr (FMT == F_BF16) {
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][tm], bfr[ks & 1][tn], acc[tm][tn], 0, 0, 0);
             } else {
-              i32x4 v4 = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
-              bfr[tn] = (i32x8){v4[0], v4[1], v4[2], v4[3], 0, 0, 0, 0};
-            }
-          }
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-              int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
+              const int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
+              const int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
               acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[tm], bfr[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
+                  af[ks & 1][tm], bfr[ks & 1][tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
             }
           }
         }
       }
+      stage_hint<C::STEPS, READS + (C::SCALED ? TM + TN : 0), READS, TM * TN,
+                 G::A_INSTR + G::B_INSTR + (C::SCALED ? 2 : 0)>();
     }
 
     // ---- epilogue.  Accumulator element v of lane l is row
@@ -252,16 +307,17 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
 #pragma unroll
         for (int pp = 0; pp < TN / 2; ++pp) {
           const int icol = nb * (GEMM_BN / 2) + (wn * (TN / 2) + pp) * 32 + l32;
+          const int row0 = m0 + wm * TM * 32 + tm * 32 + 4 * g;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-            float a = act_swiglu(acc[tm][2 * pp][v], acc[tm][2 * pp + 1][v], p);
+            const int row = row0 + 8 * (v >> 2) + (v & 3);
+            const float a = act_swiglu(acc[tm][2 * pp][v], acc[tm][2 * pp + 1][v], p);
             if constexpr (FMT == F_BF16) {
               ((uint16_t*)(p.c + (int64_t)row * p.c_ld))[icol] = bf16_rne(a);
             } else {
               // MXFP8 L2 input: one UE8M0 scale per 32 intermediate columns,
               // which are exactly the 32 lanes of this half-wave.
-              float amax = group_max<5>(__builtin_fabsf(a));
+              const float amax = group_max<5>(__builtin_fabsf(a));
               uint32_t q = 0;
               int c = 0;
               if (amax > 0.0f) {
@@ -272,6 +328,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
               if (l32 == 0) p.c_sf[(int64_t)row * p.c_sf_ld + (icol >> 5)] = (uint8_t)c;
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
@@ -282,9 +339,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) k_gemm(const GemmArgs p) {
           const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
           const int slot = p.sorted_slot[row];
           if (slot < 0) continue;
-          float* orow = p.o + (int64_t)slot * p.N;
+          float* orow = p.o + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) orow[nb * GEMM_BN + (wn * TN + tn) * 32 + l32] = acc[tm][tn][v];
+          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = acc[tm][tn][v];
         }
       }
     }
