@@ -65,9 +65,10 @@ struct TileGeom {
   static constexpr int TN = GEMM_BN / WN / 32;
   static constexpr int A_STAGE = BM * C::A_ROW;
   static constexpr int B_STAGE = GEMM_BN * C::B_ROW;
-  static constexpr int A_SF_ROWS = BM < 64 ? 64 : BM;
-  static constexpr int A_SF_STAGE = C::SCALED ? A_SF_ROWS * 4 : 0;
-  static constexpr int B_SF_STAGE = C::SCALED ? (GEMM_BN / 32) * 128 : 0;
+  // every wave copies 64 rows of A scales (rows wrap modulo BM) and its own
+  // copy of the 1 KiB of B scales, so the copy code has no wave branches
+  static constexpr int A_SF_STAGE = C::SCALED ? 4 * 256 : 0;
+  static constexpr int B_SF_STAGE = C::SCALED ? 4 * (GEMM_BN / 32) * 128 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
@@ -122,34 +123,41 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
   }
 }
 
-// Scheduling hint for one K stage, as an ordered list of instruction groups:
-// the first K-step's LDS reads (FIRST), then MFMA by MFMA: after MFMA j of
-// K-step ks (ks < STEPS - 1) its share of the next step's READS reads, and,
-// over the first half of the stage, its share of the VMEM global->LDS copies
-// for the next stage, so no wave stalls issuing a burst of copies.
-template <int J, int STEPS, int READS, int MFMAS, int VMEM>
-__device__ __forceinline__ void stage_mfma_hint() {
-  constexpr int TOTAL = STEPS * MFMAS;
-  if constexpr (J < TOTAL) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int ks = J / MFMAS, i = J % MFMAS;
-    if constexpr (ks + 1 < STEPS) {
-      constexpr int r = ((i + 1) * READS) / MFMAS - (i * READS) / MFMAS;
-      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-    }
-    constexpr int HALF = TOTAL / 2 > 0 ? TOTAL / 2 : 1;
-    if constexpr (J < HALF) {
-      constexpr int v = ((J + 1) * VMEM) / HALF - (J * VMEM) / HALF;
-      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
-    }
-    stage_mfma_hint<J + 1, STEPS, READS, MFMAS, VMEM>();
+// Scheduling hints.  interleave_hint: READS LDS reads spread between MFMAS
+// MFMAs, one read followed by its share of the MFMAs.
+template <int I, int READS, int MFMAS>
+__device__ __forceinline__ void interleave_hint() {
+  if constexpr (I < READS) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr int q = ((I + 1) * MFMAS) / READS - (I * MFMAS) / READS;
+    if constexpr (q > 0) __builtin_amdgcn_sched_group_barrier(0x008, q, 0);
+    interleave_hint<I + 1, READS, MFMAS>();
   }
 }
 
-template <int STEPS, int FIRST, int READS, int MFMAS, int VMEM>
-__device__ __forceinline__ void stage_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
-  stage_mfma_hint<0, STEPS, READS, MFMAS, VMEM>();
+// boundary_hint: after the barrier, the next stage's first reads are spread
+// over the first half of the last K-step's MFMAs and the copies of stage s+2
+// over the second half.
+template <int I, int READS, int MFMAS, int VMEM>
+__device__ __forceinline__ void boundary_mfma_hint() {
+  if constexpr (I < MFMAS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int H = MFMAS / 2 > 0 ? MFMAS / 2 : 1;
+    if constexpr (I < H) {
+      constexpr int r = ((I + 1) * READS) / H - (I * READS) / H;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    } else {
+      constexpr int J = I - H, H2 = MFMAS - H > 0 ? MFMAS - H : 1;
+      constexpr int v = ((J + 1) * VMEM) / H2 - (J * VMEM) / H2;
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);
+    }
+    boundary_mfma_hint<I + 1, READS, MFMAS, VMEM>();
+  }
+}
+
+template <int READS, int MFMAS, int VMEM>
+__device__ __forceinline__ void boundary_hint() {
+  boundary_mfma_hint<0, READS, MFMAS, VMEM>();
 }
 
 template <int FMT, int BM, int LAYER>
@@ -202,7 +210,6 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
       a_off[i] = row * p.a_ld + (swz(r, lane & 7) << 4);
     }
     int64_t asf_off = 0;
-    const bool asf_wave = C::SCALED && (w * 64 < BM || w == 0);
     if constexpr (C::SCALED) {
       const int r = (w * 64 + lane) % BM;
       int64_t row;
@@ -231,15 +238,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         g2lds16(src, st + G::A_STAGE + q * 1024);
       }
       if constexpr (C::SCALED) {
-        // A scales: this stage's 4 UE8M0 bytes of every row
-        if (asf_wave)
-          __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
-                                           (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
-        // B scales: [32-row block][stage][64 lanes x 2 K-steps]
-        if (w == 0) {
-          const uint8_t* src = wsf + ((int64_t)(nb * 8 + (lane >> 3)) * nstages + s) * 128 + (lane & 7) * 16;
-          g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE);
-        }
+        // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
+        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
+                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
+        // B scales: [32-row block][stage][64 lanes x 2 K-steps], one copy per wave
+        const uint8_t* src = wsf + ((int64_t)(nb * 8 + (lane >> 3)) * nstages + s) * 128 + (lane & 7) * 16;
+        g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
       }
     };
 
@@ -251,21 +255,14 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // the previous tile's copies have landed and its readers are done with
-    // both buffers
-    wait_vmcnt0();
-    __syncthreads();
-    issue(0, 0);
-    for (int s = 0; s < nstages; ++s) {
-      wait_vmcnt0();
-      __syncthreads();
-      // unconditional, so the copies share a scheduling region with the
-      // MFMAs; the last stage re-copies itself into the idle buffer
-      issue(s + 1 < nstages ? s + 1 : s, (s + 1) & 1);
-      const uint8_t* st = smem + (s & 1) * G::STAGE;
-      const uint8_t* As = st;
-      const uint8_t* Bs = st + G::A_STAGE;
-      uint32_t sa4[TM], sb2[TN];
+    // Stage s lives in LDS buffer s & 1.  Stage s+1's copy is issued while
+    // stage s computes; each stage's wait + barrier sits just before its last
+    // K-step, so the next stage's first fragments are read while the last
+    // K-step's MFMAs run and no LDS latency follows the barrier.  Copies are
+    // issued unconditionally (stage indices clamped to the last stage, an
+    // in-bounds re-copy into the idle buffer) so they share a scheduling
+    // region with the MFMAs; the next tile drains them before reusing LDS.
+    auto read_scales = [&](const uint8_t* st, uint32_t (&sa4)[TM], uint32_t (&sb2)[TN]) {
       if constexpr (C::SCALED) {
         const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
         const uint8_t* Bsf = Asf + G::A_SF_STAGE;
@@ -274,29 +271,58 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) sb2[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
       }
-      FA af[2][TM];
-      FB bfr[2][TN];
-      load_frags<FMT, TM, TN>(As, Bs, 0, wm, wn, lane, af[0], bfr[0]);
+    };
+    auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa4)[TM],
+                     const uint32_t (&sb2)[TN]) {
 #pragma unroll
-      for (int ks = 0; ks < C::STEPS; ++ks) {
-        if (ks + 1 < C::STEPS) load_frags<FMT, TM, TN>(As, Bs, ks + 1, wm, wn, lane, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            if constexpr (FMT == F_BF16) {
-              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][tm], bfr[ks & 1][tn], acc[tm][tn], 0, 0, 0);
-            } else {
-              const int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
-              const int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
-              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[ks & 1][tm], bfr[ks & 1][tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
-            }
+        for (int tn = 0; tn < TN; ++tn) {
+          if constexpr (FMT == F_BF16) {
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+          } else {
+            const int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
+            const int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
           }
         }
       }
-      stage_hint<C::STEPS, READS + (C::SCALED ? TM + TN : 0), READS, TM * TN,
-                 G::A_INSTR + G::B_INSTR + (C::SCALED ? 2 : 0)>();
+    };
+
+    wait_vmcnt0();
+    __syncthreads();          // the previous tile's copies and reads are done
+    issue(0, 0);
+    wait_vmcnt0();
+    __syncthreads();
+    issue(nstages > 1 ? 1 : 0, 1);
+    FA af[2][TM];
+    FB bfr[2][TN];
+    uint32_t sa4[TM] = {}, sb2[TN] = {}, sa4n[TM] = {}, sb2n[TN] = {};
+    read_scales(smem, sa4, sb2);
+    load_frags<FMT, TM, TN>(smem, smem + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
+    for (int s = 0; s < nstages; ++s) {
+      const uint8_t* st = smem + (s & 1) * G::STAGE;
+#pragma unroll
+      for (int ks = 0; ks + 1 < C::STEPS; ++ks) {
+        load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+        mfmas(ks, af[ks & 1], bfr[ks & 1], sa4, sb2);
+        interleave_hint<0, READS, TM * TN>();
+      }
+      // stage boundary: stage s+1 has landed and every wave is done reading
+      // stage s, whose buffer then takes stage s+2
+      wait_vmcnt0();
+      __syncthreads();
+      const uint8_t* nx = smem + ((s + 1) & 1) * G::STAGE;
+      read_scales(nx, sa4n, sb2n);
+      load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
+      issue(s + 2 < nstages ? s + 2 : nstages - 1, s & 1);
+      mfmas(C::STEPS - 1, af[(C::STEPS - 1) & 1], bfr[(C::STEPS - 1) & 1], sa4, sb2);
+      boundary_hint<READS + (C::SCALED ? TM + TN : 0), TM * TN, G::A_INSTR + G::B_INSTR + (C::SCALED ? 2 : 0)>();
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) sa4[tm] = sa4n[tm];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
     }
 
     // ---- epilogue.  Accumulator element v of lane l is row
