@@ -229,20 +229,20 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
       for (int i = 0; i < G::A_INSTR; ++i)
         g2lds16(p.a + a_off[i] + s * C::A_ROW, st + (w * G::A_INSTR + i) * 1024);
-      // weight fragments: [32-row block][stage][B_ROW * 32 bytes] per expert
+      // weight fragments: [stage][32-row block][B_ROW * 32 bytes] per expert
 #pragma unroll
       for (int i = 0; i < G::B_INSTR; ++i) {
         const int q = w * G::B_INSTR + i;
         const int nf = q / G::B_FRAGS_PER_NF, sub = q % G::B_FRAGS_PER_NF;
-        const uint8_t* src = wexp + ((int64_t)(nb * 8 + nf) * nstages + s) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
+        const uint8_t* src = wexp + ((int64_t)s * (p.N / 32) + nb * 8 + nf) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
         g2lds16(src, st + G::A_STAGE + q * 1024);
       }
       if constexpr (C::SCALED) {
         // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
         __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
                                          (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
-        // B scales: [32-row block][stage][64 lanes x 2 K-steps], one copy per wave
-        const uint8_t* src = wsf + ((int64_t)(nb * 8 + (lane >> 3)) * nstages + s) * 128 + (lane & 7) * 16;
+        // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
+        const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
         g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
       }
     };

@@ -15,10 +15,13 @@
 //                     in bytes 16-31 of lane group g)
 //   FP4  (32x32x64):  1 KiB, lane l = row l%32, bytes [32ks + 16(l/32), +16)
 //                     (4-bit operands hold K [32g, 32g+32) contiguously)
-// Fragments are ordered [32-row block][K-step].  UE8M0 scales become
-// [32-row block][128-K stage][lane][2]: byte j of lane l is the scale of row
-// l%32, block 4*stage + 2j + l/32, the byte the scaled MFMA of K-step j takes
-// from that lane.
+// Fragments are ordered [K stage][32-row block][K-step within the stage]
+// (a stage is 64 K for BF16, 128 K otherwise), so the 8 blocks one tile reads
+// in a stage, and the blocks of neighbouring tiles, are contiguous rather than
+// a large power-of-two stride apart on the same memory channel.  UE8M0 scales
+// become [128-K stage][32-row block][lane][2]: byte j of lane l is the scale
+// of row l%32, block 4*stage + 2j + l/32, the byte the scaled MFMA of K-step
+// j takes from that lane.
 #include "common.h"
 #include "launch.h"
 
@@ -34,27 +37,28 @@ __global__ void __launch_bounds__(256) k_transform_codes(const uint8_t* __restri
   const int64_t e = c / chunks_per_expert, ce = c % chunks_per_expert;
   int n, kbyte;
   int64_t row_bytes;
+  const int nfs = N / 32;
   if (FMT == F_BF16) {
-    const int64_t f = ce >> 6;
+    const int64_t f = ce >> 6;                  // [stage][nf][4 K-steps of 16]
     const int l = (int)(ce & 63);
-    const int ksteps = K / 16;
-    const int nf = (int)(f / ksteps), ks = (int)(f % ksteps);
+    const int64_t rest = f >> 2;
+    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 4 + (int)(f & 3);
     n = nf * 32 + (l & 31);
     kbyte = ks * 32 + (l >> 5) * 16;
     row_bytes = (int64_t)K * 2;
   } else if (FMT == F_MXFP8) {
-    const int64_t f = ce >> 7;
+    const int64_t f = ce >> 7;                  // [stage][nf][2 K-steps of 64]
     const int within = (int)(ce & 127), j = within >> 6, l = within & 63;
-    const int ksteps = K / 64;
-    const int nf = (int)(f / ksteps), ks = (int)(f % ksteps);
+    const int64_t rest = f >> 1;
+    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 2 + (int)(f & 1);
     n = nf * 32 + (l & 31);
     kbyte = ks * 64 + 32 * j + 16 * (l >> 5);
     row_bytes = K;
   } else {  // FP4
-    const int64_t f = ce >> 6;
+    const int64_t f = ce >> 6;                  // [stage][nf][2 K-steps of 64]
     const int l = (int)(ce & 63);
-    const int ksteps = K / 64;
-    const int nf = (int)(f / ksteps), ks = (int)(f % ksteps);
+    const int64_t rest = f >> 1;
+    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 2 + (int)(f & 1);
     n = nf * 32 + (l & 31);
     kbyte = ks * 32 + 16 * (l >> 5);
     row_bytes = K / 2;
@@ -72,10 +76,9 @@ __global__ void __launch_bounds__(256) k_transform_mx_scales(const uint8_t* __re
   if (i >= total) return;
   const int64_t per_expert = (int64_t)N * (K / 32);
   const int64_t e = i / per_expert, r = i % per_expert;
-  const int nstages = K / 128;
-  const int64_t blk = r / 128;             // (nf, stage) block of 128 bytes
+  const int64_t blk = r / 128;             // (stage, nf) block of 128 bytes
   const int within = (int)(r % 128), l = within >> 1, j = within & 1;
-  const int nf = (int)(blk / nstages), stage = (int)(blk % nstages);
+  const int nf = (int)(blk % (N / 32)), stage = (int)(blk / (N / 32));
   const int n = nf * 32 + (l & 31);
   const int kb = stage * 4 + 2 * j + (l >> 5);
   const int srow = W13 ? w13_canonical_row(n, inter) : n;
