@@ -112,7 +112,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
 bool valid_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == MOE_FMT_MXFP4 || f == MOE_FMT_NVFP4; }
 
 // Formats whose grouped GEMMs this build implements.
-bool gemm_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == MOE_FMT_MXFP4; }
+bool gemm_fmt(int f) { return valid_fmt(f); }
 
 int block_m_rule(int T, int n_loc, int n_sh, int k) {
   const double expected = (double)T * (k + n_sh) / (double)(n_loc + n_sh);
@@ -282,6 +282,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   mark(2 * MOE_STEP_QUANT_X);
   if (fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4)
     launch_quant_mx(false, false, T, (int)H, x, w.xq, w.xq_sf, s);
+  else if (fmt == MOE_FMT_NVFP4)
+    launch_quant_nv(false, T, (int)H, x, w.xq, w.xq_sf, w.x_tok, nullptr, 1, s);
   mark(2 * MOE_STEP_QUANT_X + 1);
   // a2: routing metadata
   mark(2 * MOE_STEP_DISPATCH);
@@ -294,20 +296,24 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   const int64_t ebytes = fmt == MOE_FMT_BF16 ? 2 : 1;  // bytes per element (codes); FP4 below
+  const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
+  const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (fmt == MOE_FMT_BF16) {
     g.a = (const uint8_t*)x;
     g.a_ld = H * 2;
   } else {
     g.a = w.xq;
-    g.a_ld = H;
+    g.a_ld = nv ? H / 2 : H;
     g.a_sf = w.xq_sf;
-    g.a_sf_ld = H / 32;
+    g.a_sf_ld = H / grp;
+    g.a_tok = w.x_tok;
   }
   g.w = (const uint8_t*)w13_k;
   g.w_sf = (const uint8_t*)w13_sf_k;
+  g.w_gs = w13_gscale;
   const int64_t w13_elems = 2 * I * H, w2_elems = H * I;
-  g.w_expert_bytes = fmt == MOE_FMT_MXFP4 ? w13_elems / 2 : w13_elems * ebytes;
-  g.w_sf_expert_bytes = scaled ? w13_elems / 32 : 0;
+  g.w_expert_bytes = fp4 ? w13_elems / 2 : w13_elems * ebytes;
+  g.w_sf_expert_bytes = scaled ? w13_elems / grp : 0;
   g.N = (int)(2 * I);
   g.K = (int)H;
   g.sorted_slot = w.sorted_slot;
@@ -317,8 +323,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.kk = (int)kk;
   g.c = w.a2;
   g.c_sf = w.a2_sf;
-  g.c_ld = fmt == MOE_FMT_BF16 ? I * 2 : I;
-  g.c_sf_ld = I / 32;
+  g.c_ld = fmt == MOE_FMT_BF16 ? I * 2 : (nv ? I / 2 : I);
+  g.c_sf_ld = I / grp;
   g.inter = (int)I;
   g.has_clamp = a.has_clamp;
   g.clamp = a.clamp;
@@ -335,11 +341,13 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g2.a = w.a2;
   g2.a_ld = g.c_ld;
   g2.a_sf = w.a2_sf;
-  g2.a_sf_ld = I / 32;
+  g2.a_sf_ld = I / grp;
+  g2.a_tok = nullptr;
   g2.w = (const uint8_t*)w2_k;
   g2.w_sf = (const uint8_t*)w2_sf_k;
-  g2.w_expert_bytes = fmt == MOE_FMT_MXFP4 ? w2_elems / 2 : w2_elems * ebytes;
-  g2.w_sf_expert_bytes = scaled ? w2_elems / 32 : 0;
+  g2.w_gs = w2_gscale;
+  g2.w_expert_bytes = fp4 ? w2_elems / 2 : w2_elems * ebytes;
+  g2.w_sf_expert_bytes = scaled ? w2_elems / grp : 0;
   g2.N = (int)H;
   g2.K = (int)I;
   g2.o = w.o;

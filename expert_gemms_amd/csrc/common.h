@@ -93,6 +93,50 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return (c & 0x80) ? -mag : mag;
 }
 
+// E4M3 byte -> float32: the exponent and mantissa fields moved into the
+// float32 fields and rebiased by 2^120 (subnormal codes land on float32
+// subnormals first, so every code is exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return u2f(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20)) * 0x1p120f;
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// An E4M3 block scale split for gfx950's packed FP4 convert, which applies
+// only the power of two of its float32 scale: bs = pow2 * mult with
+// pow2 = 2^(e-7), mult = 1 + m/8 (normal codes) or pow2 = 2^-9, mult = m
+// (subnormal codes).
+struct NvScale {
+  float pow2;
+  f16x2 mult;
+};
+__device__ __forceinline__ NvScale nv_scale(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  NvScale s;
+  s.pow2 = e ? u2f((e + 120u) << 23) : 0x1p-9f;
+  const _Float16 h = e ? (_Float16)(1.0f + (float)m * 0.125f) : (_Float16)(float)m;
+  s.mult = (f16x2){h, h};
+  return s;
+}
+
+// Eight packed E2M1 values (one dword, two per byte, element 2b in the low
+// nibble of byte b) times an E4M3 block scale -> eight FP16 values.  The
+// convert scales by the power of two; the packed FP16 multiply adds the
+// mantissa.  E2M1 x E4M3 has at most 6 significant bits and magnitudes in
+// [2^-10, 2688], so both steps are exact in FP16.  The vector is assembled
+// by bit casts of whole dwords.
+__device__ __forceinline__ f16x8 nvfp4_to_f16x8(int packed, const NvScale& s) {
+  const uint32_t v = (uint32_t)packed;
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s.pow2, 0) * s.mult;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s.pow2, 1) * s.mult;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s.pow2, 2) * s.mult;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s.pow2, 3) * s.mult;
+  const i32x4 w = {__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1), __builtin_bit_cast(int, p2),
+                   __builtin_bit_cast(int, p3)};
+  return __builtin_bit_cast(f16x8, w);
+}
+
 // UE8M0 code of an MX block from its float32 amax (> 0): the smallest e with
 // amax <= fmax * 2^e, code 127 + e clamped to [1, 254].  With amax = m * 2^p:
 // E4M3 (fmax = 1.75 * 2^8): e = p - 8 + [m > 1.75];  E2M1 (1.5 * 2^2):

@@ -8,7 +8,10 @@
 // DeepGemmExperts.apply (grouped GEMM, activation, per-group quantisation,
 // grouped GEMM).  Weight formats: BF16 (32x32x16 bf16 MFMA), MXFP8 and MXFP4
 // (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4 consuming the UE8M0 block scales
-// directly; MXFP4 weights against MXFP8 activations).
+// directly; MXFP4 weights against MXFP8 activations), NVFP4 (E2M1 operands
+// with E4M3 block scales, dequantised to exact FP16 in registers and fed to
+// the 32x32x16 f16 MFMA; per-token and per-expert FP32 scales in the
+// epilogues).
 //
 // Work decomposition: a persistent grid of (#CUs) workgroups walks the tiles
 // (BLOCK_M rows of one expert x 256 output columns).  Every tile has the same
@@ -34,17 +37,24 @@
 namespace moe {
 
 template <int FMT> struct FmtCfg;
+// KSTAGE: K elements per LDS stage; A_ROW / B_ROW: bytes per row per stage;
+// STEPS: register-fragment steps per stage (an MFMA K-step, or for NVFP4 a
+// 64-K group of four BF16 K-steps).
 template <> struct FmtCfg<F_BF16> {
   static constexpr int KSTAGE = 64, A_ROW = 128, B_ROW = 128, STEPS = 4;
-  static constexpr bool SCALED = false;
+  static constexpr bool SCALED = false, NV = false;
 };
 template <> struct FmtCfg<F_MXFP8> {
   static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 128, STEPS = 2;
-  static constexpr bool SCALED = true;
+  static constexpr bool SCALED = true, NV = false;
 };
 template <> struct FmtCfg<F_MXFP4> {
   static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 64, STEPS = 2;
-  static constexpr bool SCALED = true;
+  static constexpr bool SCALED = true, NV = false;
+};
+template <> struct FmtCfg<F_NVFP4> {
+  static constexpr int KSTAGE = 128, A_ROW = 64, B_ROW = 64, STEPS = 2;
+  static constexpr bool SCALED = true, NV = true;
 };
 
 __device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
@@ -63,32 +73,44 @@ struct TileGeom {
   static constexpr int WN = 4 / WM;
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = GEMM_BN / WN / 32;
-  static constexpr int A_STAGE = BM * C::A_ROW;
+  // every wave issues at least one A copy (rows wrap modulo BM)
+  static constexpr int A_STAGE = BM * C::A_ROW < 4096 ? 4096 : BM * C::A_ROW;
   static constexpr int B_STAGE = GEMM_BN * C::B_ROW;
-  // every wave copies 64 rows of A scales (rows wrap modulo BM) and its own
-  // copy of the 1 KiB of B scales, so the copy code has no wave branches
-  static constexpr int A_SF_STAGE = C::SCALED ? 4 * 256 : 0;
-  static constexpr int B_SF_STAGE = C::SCALED ? 4 * (GEMM_BN / 32) * 128 : 0;
+  // every wave copies 64 rows of A scales (rows wrap modulo BM; NVFP4: two
+  // halves of 4 bytes) and its own B scales, so the copy code has no wave
+  // branches
+  static constexpr int A_SF_STAGE = C::SCALED ? (C::NV ? 2 : 1) * 4 * 256 : 0;
+  static constexpr int B_SF_STAGE = C::SCALED ? 4 * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int ROWS_OFF = 2 * STAGE;            // per-row epilogue scales (NVFP4)
+  static constexpr int LDS = 2 * STAGE + (C::NV ? 1024 : 0);
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
   static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // per wave
+  static constexpr int A_RPI = 1024 / C::A_ROW;         // A rows per copy instruction
+  static constexpr int A_CPR = C::A_ROW / 16;           // 16-byte chunks per A row
   static constexpr int B_FRAGS_PER_NF = C::B_ROW * 32 / 1024;
   static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small");
   static_assert(TN % 2 == 0, "gate/up pairs need an even number of N fragments");
 };
 
-// LDS A rows are 128 bytes (8 chunks of 16 bytes).  gfx950 LDS serves 16
-// lanes x 16 bytes per cycle from 64 banks, so the 16 rows a ds_read_b128
-// phase touches must land on 16 distinct 16-byte bank groups: rows r and r+1
-// already differ by 128 bytes, so the chunk index is XORed with (r >> 1) & 7.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// LDS A rows are 128 bytes (8 chunks of 16 bytes) or, for NVFP4, 64 bytes
+// (4 chunks).  gfx950 LDS serves 16 lanes x 16 bytes per cycle from 64 banks,
+// so the 16 rows a ds_read_b128 phase touches must land on 16 distinct
+// 16-byte bank groups: the chunk index is XORed with (r >> 1) & 7 for
+// 128-byte rows (rows r, r+1 already differ by 128 bytes) and with
+// (r >> 2) & 3 for 64-byte rows.
+template <int A_ROW>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (A_ROW == 128) return c ^ ((r >> 1) & 7);
+  else return c ^ ((r >> 2) & 3);
+}
 
 // MFMA operand fragments of one K-step.
 template <int FMT> struct Frag;
 template <> struct Frag<F_BF16> { using A = bf16x8; using B = bf16x8; };
 template <> struct Frag<F_MXFP8> { using A = i32x8; using B = i32x8; };
 template <> struct Frag<F_MXFP4> { using A = i32x8; using B = i32x8; };
+template <> struct Frag<F_NVFP4> { using A = i32x4; using B = i32x4; };   // raw E2M1, 32 values
 
 template <int FMT, int TM, int TN>
 __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int ks, int wm, int wn, int lane,
@@ -98,12 +120,15 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
   for (int tm = 0; tm < TM; ++tm) {
     const int r = wm * TM * 32 + tm * 32 + l32;
     if constexpr (FMT == F_BF16) {
-      af[tm] = *(const bf16x8*)(As + r * 128 + (swz(r, ks * 2 + g) << 4));
+      af[tm] = *(const bf16x8*)(As + r * 128 + (swz<128>(r, ks * 2 + g) << 4));
+    } else if constexpr (FMT == F_NVFP4) {
+      // 64-K group ks: lane group g holds K [32g, 32g+32) of the group
+      af[tm] = *(const i32x4*)(As + r * 64 + (swz<64>(r, ks * 2 + g) << 4));
     } else {
       // 8-bit A operand: register bytes 0-15 hold K [16g, 16g+16) of the
       // 64-wide K-step, bytes 16-31 hold K [32+16g, +16)
-      const i32x4 lo = *(const i32x4*)(As + r * 128 + (swz(r, ks * 4 + g) << 4));
-      const i32x4 hi = *(const i32x4*)(As + r * 128 + (swz(r, ks * 4 + 2 + g) << 4));
+      const i32x4 lo = *(const i32x4*)(As + r * 128 + (swz<128>(r, ks * 4 + g) << 4));
+      const i32x4 hi = *(const i32x4*)(As + r * 128 + (swz<128>(r, ks * 4 + 2 + g) << 4));
       af[tm] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
@@ -116,6 +141,8 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
       const uint8_t* f = Bs + (nf * 2 + ks) * 2048 + lane * 16;
       const i32x4 lo = *(const i32x4*)f, hi = *(const i32x4*)(f + 1024);
       bf[tn] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else if constexpr (FMT == F_NVFP4) {
+      bf[tn] = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
     } else {
       const i32x4 v = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
       bf[tn] = (i32x8){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
@@ -167,7 +194,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   using FA = typename Frag<FMT>::A;
   using FB = typename Frag<FMT>::B;
   constexpr int TM = G::TM, TN = G::TN;
-  constexpr int READS = TM * (FMT == F_BF16 ? 1 : 2) + TN * (FMT == F_MXFP8 ? 2 : 1);
+  constexpr int READS = FMT == F_NVFP4 ? TM + TN : TM * (FMT == F_BF16 ? 1 : 2) + TN * (FMT == F_MXFP8 ? 2 : 1);
+  constexpr int SA_N = C::NV ? 2 * TM : TM;   // A-scale dwords held per stage
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -195,11 +223,13 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
     const int m0 = (mb0 + local % mcount) * BM;
 
     // ---- per-lane A row offsets for the LDS-DMA copies: lane l of copy i
-    // fills LDS row r = 8 * (copy index) + l / 8, physical chunk l % 8
+    // fills LDS row r = A_RPI * (copy index) + l / A_CPR, physical chunk
+    // l % A_CPR (rows wrap modulo BM when a wave has more lanes than rows)
     int64_t a_off[G::A_INSTR];
 #pragma unroll
     for (int i = 0; i < G::A_INSTR; ++i) {
-      const int r = (w * G::A_INSTR + i) * 8 + (lane >> 3);
+      const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
+      const int r = rl % BM;
       int64_t row;
       if (LAYER == 1) {
         const int s = p.sorted_slot[m0 + r];
@@ -207,7 +237,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
       } else {
         row = m0 + r;
       }
-      a_off[i] = row * p.a_ld + (swz(r, lane & 7) << 4);
+      a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
     }
     int64_t asf_off = 0;
     if constexpr (C::SCALED) {
@@ -237,12 +267,23 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         const uint8_t* src = wexp + ((int64_t)s * (p.N / 32) + nb * 8 + nf) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
         g2lds16(src, st + G::A_STAGE + q * 1024);
       }
-      if constexpr (C::SCALED) {
+      if constexpr (C::SCALED && !C::NV) {
         // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
         __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
                                          (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
         // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
         const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
+        g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
+      } else if constexpr (C::NV) {
+        // A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM), as two
+        // halves of 4 (64-K group 0, group 1)
+        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8,
+                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8 + 4,
+                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 + w * 256), 4, 0, 0);
+        // B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
+        const int byte = (lane * 16) % (TN * 256);
+        const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
         g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
       }
     };
@@ -262,29 +303,65 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
     // issued unconditionally (stage indices clamped to the last stage, an
     // in-bounds re-copy into the idle buffer) so they share a scheduling
     // region with the MFMAs; the next tile drains them before reusing LDS.
-    auto read_scales = [&](const uint8_t* st, uint32_t (&sa4)[TM], uint32_t (&sb2)[TN]) {
+    auto read_scales = [&](const uint8_t* st, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN]) {
       if constexpr (C::SCALED) {
         const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
         const uint8_t* Bsf = Asf + G::A_SF_STAGE;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) sa4[tm] = *(const uint32_t*)(Asf + (wm * TM * 32 + tm * 32 + l32) * 4);
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) sb2[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
-      }
-    };
-    auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa4)[TM],
-                     const uint32_t (&sb2)[TN]) {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
+        for (int tm = 0; tm < TM; ++tm) {
+          const int r = wm * TM * 32 + tm * 32 + l32;
+          sa[tm] = *(const uint32_t*)(Asf + r * 4);
+          if constexpr (C::NV) sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
+        }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          if constexpr (FMT == F_BF16) {
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
-          } else {
-            const int sa = (sa4[tm] >> (8 * (ks * 2 + g))) & 0xFF;
-            const int sb = (sb2[tn] >> (8 * ks)) & 0xFF;
-            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sa, 0, sb);
+          if constexpr (C::NV) sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
+          else sb[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
+        }
+      }
+    };
+    auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
+                     const uint32_t (&sb)[TN]) {
+      if constexpr (C::NV) {
+        // 64-K group ks: four 16-wide K-steps; sub-step j takes the lane's
+        // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
+        // group: byte 2g + j/2 of the row's A-scale dword, byte 2ks + j/2 of
+        // the lane's B-scale dword
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
+          NvScale ssa[TM], ssb[TN];
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * (2 * g + h))) & 0xFF);
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) ssb[tn] = nv_scale((sb[tn] >> (8 * (2 * ks + h))) & 0xFF);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * h + jj;
+            f16x8 a8[TM], b8[TN];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) a8[tm] = nvfp4_to_f16x8(af[tm][j], ssa[tm]);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) b8[tn] = nvfp4_to_f16x8(bf[tn][j], ssb[tn]);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+              for (int tn = 0; tn < TN; ++tn)
+                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[tm], b8[tn], acc[tm][tn], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            if constexpr (FMT == F_BF16) {
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+            } else {
+              const int sav = (sa[tm] >> (8 * (ks * 2 + g))) & 0xFF;
+              const int sbv = (sb[tn] >> (8 * ks)) & 0xFF;
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sav, 0, sbv);
+            }
           }
         }
       }
@@ -292,13 +369,21 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 
     wait_vmcnt0();
     __syncthreads();          // the previous tile's copies and reads are done
+    // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
+    // (read after the K loop's barriers)
+    if constexpr (C::NV && LAYER == 1) {
+      if (tid < BM) {
+        const int sl = p.sorted_slot[m0 + tid];
+        ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[e];
+      }
+    }
     issue(0, 0);
     wait_vmcnt0();
     __syncthreads();
     issue(nstages > 1 ? 1 : 0, 1);
     FA af[2][TM];
     FB bfr[2][TN];
-    uint32_t sa4[TM] = {}, sb2[TN] = {}, sa4n[TM] = {}, sb2n[TN] = {};
+    uint32_t sa4[SA_N] = {}, sb2[TN] = {}, sa4n[SA_N] = {}, sb2n[TN] = {};
     read_scales(smem, sa4, sb2);
     load_frags<FMT, TM, TN>(smem, smem + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
     for (int s = 0; s < nstages; ++s) {
@@ -307,7 +392,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
       for (int ks = 0; ks + 1 < C::STEPS; ++ks) {
         load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
         mfmas(ks, af[ks & 1], bfr[ks & 1], sa4, sb2);
-        interleave_hint<0, READS, TM * TN>();
+        interleave_hint<0, READS, TM * TN * (C::NV ? 4 : 1)>();
       }
       // stage boundary: stage s+1 has landed and every wave is done reading
       // stage s, whose buffer then takes stage s+2
@@ -318,9 +403,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
       load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
       issue(s + 2 < nstages ? s + 2 : nstages - 1, s & 1);
       mfmas(C::STEPS - 1, af[(C::STEPS - 1) & 1], bfr[(C::STEPS - 1) & 1], sa4, sb2);
-      boundary_hint<READS + (C::SCALED ? TM + TN : 0), TM * TN, G::A_INSTR + G::B_INSTR + (C::SCALED ? 2 : 0)>();
+      boundary_hint<READS + (C::SCALED ? SA_N + TN : 0), TM * TN * (C::NV ? 4 : 1), G::A_INSTR + G::B_INSTR + (C::SCALED ? (C::NV ? 3 : 2) : 0)>();
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) sa4[tm] = sa4n[tm];
+      for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
     }
@@ -337,8 +422,31 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int row = row0 + 8 * (v >> 2) + (v & 3);
-            const float a = act_swiglu(acc[tm][2 * pp][v], acc[tm][2 * pp + 1][v], p);
-            if constexpr (FMT == F_BF16) {
+            float gv = acc[tm][2 * pp][v], uv = acc[tm][2 * pp + 1][v];
+            if constexpr (C::NV) {
+              // NVFP4 accumulators carry neither the token nor the expert scale
+              const float alpha = ((const float*)(smem + G::ROWS_OFF))[row - m0];
+              gv *= alpha;
+              uv *= alpha;
+            }
+            const float a = act_swiglu(gv, uv, p);
+            if constexpr (C::NV) {
+              // NVFP4 L2 input with the one global scale g2: E4M3 scale per 16
+              // intermediate columns (16 lanes), E2M1 codes two per byte
+#pragma clang fp contract(off)
+              const float amax = group_max<4>(__builtin_fabsf(a));
+              const float six_g = 6.0f * p.l2_scale;
+              const uint32_t bs = e4m3_encode(amax / six_g);
+              const float bsv = e4m3_decode(bs);
+              uint32_t q = 0;
+              if (bsv != 0.0f) {
+                const float r = 1.0f / (bsv * p.l2_scale);
+                q = e2m1_encode(a * r);
+              }
+              const uint32_t qn = (uint32_t)shfl_xor((int)q, 1);
+              if ((l32 & 1) == 0) p.c[(int64_t)row * p.c_ld + (icol >> 1)] = (uint8_t)(q | (qn << 4));
+              if ((l32 & 15) == 0) p.c_sf[(int64_t)row * p.c_sf_ld + (icol >> 4)] = (uint8_t)bs;
+            } else if constexpr (FMT == F_BF16) {
               ((uint16_t*)(p.c + (int64_t)row * p.c_ld))[icol] = bf16_rne(a);
             } else {
               // MXFP8 L2 input: one UE8M0 scale per 32 intermediate columns,
@@ -358,6 +466,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         }
       }
     } else {
+      // NVFP4: w2's expert scale times the L2 input's global scale
+      const float alpha2 = C::NV ? p.w_gs[e] * p.l2_scale : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -367,7 +477,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
           if (slot < 0) continue;
           float* orow = p.o + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = acc[tm][tn][v];
+          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
         }
       }
     }
@@ -401,7 +511,8 @@ hipError_t gemm_init(int /*device*/) {
   hipError_t e;
   if ((e = init_fmt<F_BF16>()) != hipSuccess) return e;
   if ((e = init_fmt<F_MXFP8>()) != hipSuccess) return e;
-  return init_fmt<F_MXFP4>();
+  if ((e = init_fmt<F_MXFP4>()) != hipSuccess) return e;
+  return init_fmt<F_NVFP4>();
 }
 
 template <int FMT, int BM>
@@ -429,6 +540,7 @@ hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& a, int grid, 
     case F_BF16: return launch_fmt<F_BF16>(layer, bm, a, grid, st);
     case F_MXFP8: return launch_fmt<F_MXFP8>(layer, bm, a, grid, st);
     case F_MXFP4: return launch_fmt<F_MXFP4>(layer, bm, a, grid, st);
+    case F_NVFP4: return launch_fmt<F_NVFP4>(layer, bm, a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -85,6 +85,25 @@ __global__ void __launch_bounds__(256) k_transform_mx_scales(const uint8_t* __re
   dst[i] = src[e * per_expert + (int64_t)srow * (K / 32) + kb];
 }
 
+// NVFP4 E4M3 scales: [128-K stage][32-row block][lane][4]: byte 2*kg + i of
+// lane l is the scale of row l%32, 16-block 8*stage + 4*kg + 2*(l/32) + i,
+// i.e. the blocks of the 32 values lane group l/32 holds in 64-K group kg.
+template <bool W13>
+__global__ void __launch_bounds__(256) k_transform_nv_scales(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                             int N, int K, int inter, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t per_expert = (int64_t)N * (K / 16);
+  const int64_t e = i / per_expert, r = i % per_expert;
+  const int64_t blk = r / 256;             // (stage, nf) block of 256 bytes
+  const int within = (int)(r % 256), l = within >> 2, b = within & 3;
+  const int nf = (int)(blk % (N / 32)), stage = (int)(blk / (N / 32));
+  const int n = nf * 32 + (l & 31);
+  const int kb = stage * 8 + (b >> 1) * 4 + 2 * (l >> 5) + (b & 1);
+  const int srow = W13 ? w13_canonical_row(n, inter) : n;
+  dst[i] = src[e * per_expert + (int64_t)srow * (K / 16) + kb];
+}
+
 template <int FMT>
 static void transform_codes(int E, int N, int K, int inter, bool w13, const uint8_t* src, uint8_t* dst,
                             hipStream_t st) {
@@ -113,6 +132,17 @@ void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const ui
       transform_codes<F_MXFP4>(E, 2 * I, H, I, true, w13, w13_k, st);
       transform_codes<F_MXFP4>(E, H, I, I, false, w2, w2_k, st);
       break;
+    case F_NVFP4: {
+      // E2M1 codes share the MXFP4 fragment layout; the E4M3 scales get their own
+      transform_codes<F_MXFP4>(E, 2 * I, H, I, true, w13, w13_k, st);
+      transform_codes<F_MXFP4>(E, H, I, I, false, w2, w2_k, st);
+      const int64_t n13 = (int64_t)E * 2 * I * (H / 16), n2 = (int64_t)E * H * (I / 16);
+      hipLaunchKernelGGL((k_transform_nv_scales<true>), dim3((unsigned)((n13 + 255) / 256)), dim3(256), 0, st, w13_sf,
+                         w13_sf_k, 2 * I, H, I, n13);
+      hipLaunchKernelGGL((k_transform_nv_scales<false>), dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, w2_sf,
+                         w2_sf_k, H, I, I, n2);
+      return;
+    }
     default:
       return;
   }

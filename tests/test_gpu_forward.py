@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle.moe import moe_reference
-from synth import CONFIGS, MoEConfig, gen_routing, gen_x_bf16, bf16_bits
+from synth import CONFIGS, MoEConfig, gen_routing, gen_x_bf16, gen_w2_input_scale, bf16_bits
 from tests.gpu_util import run_layer
 from tests.helpers import check_output, make_weights
 
@@ -22,6 +22,7 @@ SMALL = {
     "mxfp8_small": MoEConfig("mxfp8_small", 12, "mxfp8", 150, 512, 256, 16, 4, num_shared=1,
                              routing="sigmoid_normal"),
     "mxfp4_small": MoEConfig("mxfp4_small", 13, "mxfp4", 37, 512, 384, 32, 8, routing="softmax_uniform"),
+    "nvfp4_small": MoEConfig("nvfp4_small", 14, "nvfp4", 300, 512, 256, 16, 6, routing="zipf"),
 }
 
 _CACHE = {}
@@ -31,16 +32,26 @@ def inputs(cfg):
     if cfg.name not in _CACHE:
         x = bf16_bits(gen_x_bf16(cfg))
         ids, wts = gen_routing(cfg)
-        if cfg.num_shared:
-            pass
         _CACHE[cfg.name] = (x, ids, wts, make_weights(cfg))
     return _CACHE[cfg.name]
 
 
+def l2_scale(cfg):
+    """NVFP4: the experts' w2 input scales and their max (1.0 if 0), the one
+    global scale every L2 input is quantised with."""
+    if cfg.fmt != "nvfp4":
+        return None, 1.0
+    w2in = gen_w2_input_scale(cfg)
+    m = float(w2in.max())
+    return w2in, (m if m > 0 else 1.0)
+
+
 def compare(cfg, block_m=0, act=None, **kw):
     x, ids, wts, w = inputs(cfg)
-    y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=block_m, act=act, **kw)
-    ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, act=act)
+    w2in, g2 = l2_scale(cfg)
+    y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=block_m, act=act,
+                     w2_input_scale=w2in, **kw)
+    ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, act=act, l2_activation_scale=g2)
     rel, excess = check_output(cfg.fmt, y, ref)
     print(f"{cfg.name} bm={block_m}: max|err|/RMS = {rel:.3e}")
     assert excess <= 0, (rel, excess)
@@ -53,7 +64,7 @@ def test_forward_matches_oracle(name):
 
 
 @pytest.mark.parametrize("bm", [32, 64, 128, 256])
-@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small"])
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small"])
 def test_forward_every_block_m(name, bm):
     compare(SMALL[name], block_m=bm)
 
@@ -90,9 +101,11 @@ def test_forward_all_dropped_and_single_token():
     assert check_output("mxfp8", y1, ref1)[1] <= 0
 
 
-def test_forward_deterministic():
-    cfg = SMALL["mxfp8_small"]
+@pytest.mark.parametrize("name", ["mxfp8_small", "nvfp4_small"])
+def test_forward_deterministic(name):
+    cfg = SMALL[name]
     x, ids, wts, w = inputs(cfg)
-    a, layer = run_layer("mxfp8", x, ids, wts, w, num_shared=1)
-    b, _ = run_layer("mxfp8", x, ids, wts, w, num_shared=1)
+    w2in, _ = l2_scale(cfg)
+    a, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
+    b, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
     assert np.array_equal(a, b)
