@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--config", default="mixtral_bf16")
     p.add_argument("--tokens", type=int, default=None, help="token count (decode workload)")
     p.add_argument("--flush-mb", type=int, default=0, help="write this many MB between steps (defeats the MALL)")
+    p.add_argument("--block-m", type=int, default=0, help="BLOCK_M (0: the library's rule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -61,6 +62,43 @@ def copy_calibration(mb, reps=3):
     print(json.dumps({"copy_mb": mb, "reps": reps, "bytes_read_per_copy": mb * (1 << 20),
                       "bytes_written_per_copy": mb * (1 << 20)}), flush=True)
     return 0
+
+
+KERNEL_SOURCES = ("expert_gemms_amd/csrc/gemm.hip", "expert_gemms_amd/csrc/common.h", "expert_gemms_amd/csrc/launch.h")
+
+
+def kernel_sha256():
+    """Hash of the GEMM kernel's sources: HBM counters taken from an older
+    kernel are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, tokens, block_m):
+    """HBM bytes per L1 launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size), or None when no summary matches the current
+    kernel sources and launch."""
+    import glob
+    sha = kernel_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "l1_gemm_hbm_*.txt"))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                k, sep, v = line.partition(": ")
+                if sep and " " not in k.strip():
+                    kv[k.strip()] = v.strip()
+        try:
+            if (kv.get("workload") == workload and int(kv["tokens"]) == tokens and int(kv["block_m"]) == block_m
+                    and kv.get("kernel_sha256") == sha):
+                return float(kv["l1_hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            continue
+    return None
 
 
 def elem_bytes(fmt):
@@ -185,7 +223,7 @@ def main():
         return evs
 
     for _ in range(args.warmup):
-        layer.forward(x, ids_d, wts_d, out=out)
+        layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
     torch.cuda.synchronize()
 
     step_events = [new_events() for _ in range(args.steps)]
@@ -197,7 +235,7 @@ def main():
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        layer.forward(x, ids_d, wts_d, out=out, step_events=step_events[i])
+        layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m, step_events=step_events[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -222,6 +260,13 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "L1 grouped GEMM"}
 
+    bm = args.block_m or layer_block_m(cfg, T)
+    traffic = profiled_traffic(cfg.name, T, bm)
+    roof["traffic"] = None if traffic is None else round(traffic / 1e9, 4)
+    roof["traffic_unit"] = "GB per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["algorithmic_per_launch"] = (round(l1_flops / 1e12, 4) if prefill else round(l1_wbytes / 1e9, 4))
+    roof["algorithmic_unit"] = "TFLOP" if prefill else "GB"
+
     cpu = None
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or min(T, 1024)
@@ -243,7 +288,7 @@ def main():
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg.name, "format": cfg.fmt, "tokens": T, "hidden": cfg.H, "inter": cfg.I,
                    "experts": cfg.E, "shared": cfg.num_shared, "top_k": cfg.top_k, "slots": S,
-                   "touched_experts": int(touched), "block_m": layer_block_m(cfg, T),
+                   "touched_experts": int(touched), "block_m": bm,
                    "flush_mb": args.flush_mb},
         "hbm_gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
