@@ -12,6 +12,8 @@
 
 #include <mutex>
 
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -114,12 +116,41 @@ bool valid_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == M
 // Formats whose grouped GEMMs this build implements.
 bool gemm_fmt(int f) { return valid_fmt(f); }
 
-int block_m_rule(int T, int n_loc, int n_sh, int k) {
-  const double expected = (double)T * (k + n_sh) / (double)(n_loc + n_sh);
-  if (expected <= 32) return 32;
-  if (expected <= 64) return 64;
-  if (expected <= 128) return 128;
-  return 256;
+// Expected padded rows of one group whose row count c is near-Poisson with
+// mean m (normal approximation): E[ceil(c / bm)] * bm = bm * sum_j P(c > j bm).
+double expected_padded(double m, int bm) {
+  if (m <= 0.0) return 0.0;
+  const double sd = std::sqrt(m);
+  double tiles = 0.0;
+  for (int j = 0;; ++j) {
+    const double x = (double)j * bm + 0.5;
+    if (x > m + 8.0 * sd + 1.0) break;
+    tiles += 0.5 * std::erfc((x - m) / (sd * 1.4142135623730951));
+  }
+  return tiles * bm;
+}
+
+// BLOCK_M from the expected group sizes (routed experts T*k/n_loc rows,
+// shared experts T): each candidate's expected padded row count is weighed by
+// the tile's relative MFMA efficiency (smaller tiles re-read more operand
+// bytes per FLOP); the cheapest wins.  NVFP4 stops at 128 (its 256-row tile
+// runs out of registers).
+int block_m_rule(int T, int n_loc, int n_sh, int k, int fmt) {
+  const double routed = (double)T * k / n_loc;
+  const int cand[4] = {32, 64, 128, 256};
+  const double eff[4] = {0.35, 0.55, 0.85, 1.0};
+  const int nc = fmt == MOE_FMT_NVFP4 ? 3 : 4;
+  int best = 32;
+  double best_cost = -1.0;
+  for (int i = 0; i < nc; ++i) {
+    const double padded = n_loc * expected_padded(routed, cand[i]) + n_sh * (double)((T + cand[i] - 1) / cand[i]) * cand[i];
+    const double cost = padded / eff[i];
+    if (best_cost < 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = cand[i];
+    }
+  }
+  return best;
 }
 
 int hip_status(hipError_t e) {
@@ -148,7 +179,7 @@ const char* moe_status_string(int status) {
 
 int moe_get_block_m(int num_tokens, int num_local_experts, int num_shared, int top_k, moe_format_t fmt) {
   if (num_tokens < 0 || num_local_experts < 1 || num_shared < 0 || top_k < 1 || !valid_fmt(fmt)) return MOE_E_INVALID;
-  return block_m_rule(num_tokens, num_local_experts, num_shared, top_k);
+  return block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
 }
 
 size_t moe_workspace_bytes(moe_format_t fmt, int max_tokens, int hidden, int inter, int num_local_experts,
@@ -264,7 +295,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   if (scaled && (!w13_sf_k || !w2_sf_k || !aligned16(w13_sf_k) || !aligned16(w2_sf_k))) return MOE_E_INVALID;
   if (fmt == MOE_FMT_NVFP4 && (!w13_gscale || !w2_gscale)) return MOE_E_INVALID;
   if (!gemm_fmt(fmt) || hidden % 256) return MOE_E_UNSUPPORTED;
-  const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k);
+  const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
   const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
   const int E = num_local_experts + num_shared;
   if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, nullptr).bytes > workspace_bytes)

@@ -170,6 +170,20 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-offs whose copies the caller has already
+// waited for with wait_vmcnt: this wave's LDS reads complete, then s_barrier.
+// (__syncthreads' release fence would also wait for every LDS-DMA copy still
+// in flight, including those of later stages.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 16-byte global -> LDS copy without a register round trip: lane l's 16
 // bytes land at `lds_base + 16 * l` (lds_base is uniform over the wave).
 __device__ __forceinline__ void g2lds16(const void* gptr, void* lds_base) {

@@ -24,13 +24,16 @@
 // Per tile: 4 waves, each owning a (BLOCK_M / WM) x (256 / WN) sub-tile of
 // 32x32 MFMA accumulators.  K advances in stages; each stage's A rows, weight
 // fragments and block scales are copied global -> LDS by the LDS-DMA path
-// (global_load_lds_dwordx4) into one of two buffers while the MFMAs consume
-// the other.  A rows sit in LDS as 128-byte rows whose 16-byte chunks are
-// XOR-swizzled (see swz) so each ds_read_b128 phase is bank-conflict free.
+// (global_load_lds_dwordx4) into a ring of LDS buffers, several stages ahead
+// of the MFMAs.  A rows sit in LDS as 64- or 128-byte rows whose 16-byte
+// chunks are XOR-swizzled (see swz) so each ds_read_b128 phase is bank-
+// conflict free.
 // Fragments of K-step ks+1 are read into a second register set while the
 // MFMAs of K-step ks run.  Weights arrive in the kernel layout written by
 // moe_transform_weights: each 32-row x K-step fragment is 1 KiB (or 2 KiB)
 // in register order, so the weight copy and its LDS reads are linear.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,21 +42,30 @@ namespace moe {
 template <int FMT> struct FmtCfg;
 // KSTAGE: K elements per LDS stage; A_ROW / B_ROW: bytes per row per stage;
 // STEPS: register-fragment steps per stage (an MFMA K-step, or for NVFP4 a
-// 64-K group of four BF16 K-steps).
+// 64-K group of four 16-wide K-steps); NBUF: LDS stage buffers (NBUF - 1
+// stages are in flight while one is computed).  Weight fragments are FRAG
+// bytes and sit in the weight layout as [layout stage][32-row block][KS_PER_L
+// K-steps], independent of how many K-steps a kernel stage takes.
 template <> struct FmtCfg<F_BF16> {
-  static constexpr int KSTAGE = 64, A_ROW = 128, B_ROW = 128, STEPS = 4;
+  static constexpr int KSTAGE = 32, A_ROW = 64, B_ROW = 64, STEPS = 2, NBUF = 4;
+  static constexpr int FRAG = 1024, KS_PER_L = 4;
   static constexpr bool SCALED = false, NV = false;
 };
+// MX formats: one 64-K scaled-MFMA step per stage; block scales keep their
+// 128-K layout stages (SC_HALF: a stage uses half of its layout stage's scales).
 template <> struct FmtCfg<F_MXFP8> {
-  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 128, STEPS = 2;
+  static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 64, STEPS = 1, NBUF = 4;
+  static constexpr int FRAG = 2048, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = false;
 };
 template <> struct FmtCfg<F_MXFP4> {
-  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 64, STEPS = 2;
+  static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 32, STEPS = 1, NBUF = 4;
+  static constexpr int FRAG = 1024, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = false;
 };
 template <> struct FmtCfg<F_NVFP4> {
-  static constexpr int KSTAGE = 128, A_ROW = 64, B_ROW = 64, STEPS = 2;
+  static constexpr int KSTAGE = 128, A_ROW = 64, B_ROW = 64, STEPS = 2, NBUF = 4;
+  static constexpr int FRAG = 1024, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = true;
 };
 
@@ -82,14 +94,21 @@ struct TileGeom {
   static constexpr int A_SF_STAGE = C::SCALED ? (C::NV ? 2 : 1) * 4 * 256 : 0;
   static constexpr int B_SF_STAGE = C::SCALED ? 4 * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
-  static constexpr int ROWS_OFF = 2 * STAGE;            // per-row epilogue scales (NVFP4)
-  static constexpr int LDS = 2 * STAGE + (C::NV ? 1024 : 0);
+  static constexpr int ROWS_OFF = C::NBUF * STAGE;      // per-row epilogue scales (NVFP4)
+  static constexpr int LDS = C::NBUF * STAGE + (C::NV ? 1024 : 0);
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
   static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // per wave
   static constexpr int A_RPI = 1024 / C::A_ROW;         // A rows per copy instruction
   static constexpr int A_CPR = C::A_ROW / 16;           // 16-byte chunks per A row
-  static constexpr int B_FRAGS_PER_NF = C::B_ROW * 32 / 1024;
+  static constexpr int B_FRAGS_PER_NF = C::B_ROW * 32 / 1024;   // 1 KiB copies per 32-row block
+  // copy instructions per wave per stage (the in-flight count of the ring)
+  static constexpr int CPS = A_INSTR + B_INSTR + (C::SCALED ? (C::NV ? 3 : 2) : 0);
   static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small");
+  static_assert(C::NBUF >= 3, "the copies of stage s + NBUF - 1 are spread over stage s");
+  static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+  // kernel stages per 128-K stage of the block-scale layouts
+  static constexpr int SPL = 128 / C::KSTAGE;
+  static_assert(!C::SCALED || C::NV || (SPL == 2 && C::STEPS == 1), "MX scale halves follow the stage parity");
   static_assert(TN % 2 == 0, "gate/up pairs need an even number of N fragments");
 };
 
@@ -112,7 +131,7 @@ template <> struct Frag<F_MXFP8> { using A = i32x8; using B = i32x8; };
 template <> struct Frag<F_MXFP4> { using A = i32x8; using B = i32x8; };
 template <> struct Frag<F_NVFP4> { using A = i32x4; using B = i32x4; };   // raw E2M1, 32 values
 
-template <int FMT, int TM, int TN>
+template <int FMT, int TM, int TN, typename C = FmtCfg<FMT>>
 __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int ks, int wm, int wn, int lane,
                                            typename Frag<FMT>::A (&af)[TM], typename Frag<FMT>::B (&bf)[TN]) {
   const int g = lane >> 5, l32 = lane & 31;
@@ -120,15 +139,15 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
   for (int tm = 0; tm < TM; ++tm) {
     const int r = wm * TM * 32 + tm * 32 + l32;
     if constexpr (FMT == F_BF16) {
-      af[tm] = *(const bf16x8*)(As + r * 128 + (swz<128>(r, ks * 2 + g) << 4));
+      af[tm] = *(const bf16x8*)(As + r * C::A_ROW + (swz<C::A_ROW>(r, ks * 2 + g) << 4));
     } else if constexpr (FMT == F_NVFP4) {
       // 64-K group ks: lane group g holds K [32g, 32g+32) of the group
-      af[tm] = *(const i32x4*)(As + r * 64 + (swz<64>(r, ks * 2 + g) << 4));
+      af[tm] = *(const i32x4*)(As + r * C::A_ROW + (swz<C::A_ROW>(r, ks * 2 + g) << 4));
     } else {
       // 8-bit A operand: register bytes 0-15 hold K [16g, 16g+16) of the
       // 64-wide K-step, bytes 16-31 hold K [32+16g, +16)
-      const i32x4 lo = *(const i32x4*)(As + r * 128 + (swz<128>(r, ks * 4 + g) << 4));
-      const i32x4 hi = *(const i32x4*)(As + r * 128 + (swz<128>(r, ks * 4 + 2 + g) << 4));
+      const i32x4 lo = *(const i32x4*)(As + r * C::A_ROW + (swz<C::A_ROW>(r, ks * 4 + g) << 4));
+      const i32x4 hi = *(const i32x4*)(As + r * C::A_ROW + (swz<C::A_ROW>(r, ks * 4 + 2 + g) << 4));
       af[tm] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
@@ -136,17 +155,28 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
   for (int tn = 0; tn < TN; ++tn) {
     const int nf = wn * TN + tn;
     if constexpr (FMT == F_BF16) {
-      bf[tn] = *(const bf16x8*)(Bs + (nf * 4 + ks) * 1024 + lane * 16);
+      bf[tn] = *(const bf16x8*)(Bs + (nf * C::STEPS + ks) * 1024 + lane * 16);
     } else if constexpr (FMT == F_MXFP8) {
-      const uint8_t* f = Bs + (nf * 2 + ks) * 2048 + lane * 16;
+      const uint8_t* f = Bs + (nf * C::STEPS + ks) * C::FRAG + lane * 16;
       const i32x4 lo = *(const i32x4*)f, hi = *(const i32x4*)(f + 1024);
       bf[tn] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else if constexpr (FMT == F_NVFP4) {
-      bf[tn] = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
+      bf[tn] = *(const i32x4*)(Bs + (nf * C::STEPS + ks) * C::FRAG + lane * 16);
     } else {
-      const i32x4 v = *(const i32x4*)(Bs + (nf * 2 + ks) * 1024 + lane * 16);
+      const i32x4 v = *(const i32x4*)(Bs + (nf * C::STEPS + ks) * C::FRAG + lane * 16);
       bf[tn] = (i32x8){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
     }
+  }
+}
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+// f(IC<I>) for I = LO .. HI-1, unrolled at compile time.
+template <int LO, int HI, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (LO < HI) {
+    f(IC<LO>{});
+    static_for<LO + 1, HI>(f);
   }
 }
 
@@ -254,38 +284,48 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
     const uint8_t* wexp = p.w + (int64_t)e * p.w_expert_bytes;
     const uint8_t* wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
 
-    auto issue = [&](int s, int buf) {
-      uint8_t* st = smem + buf * G::STAGE;
-#pragma unroll
-      for (int i = 0; i < G::A_INSTR; ++i)
-        g2lds16(p.a + a_off[i] + s * C::A_ROW, st + (w * G::A_INSTR + i) * 1024);
-      // weight fragments: [stage][32-row block][B_ROW * 32 bytes] per expert
-#pragma unroll
-      for (int i = 0; i < G::B_INSTR; ++i) {
-        const int q = w * G::B_INSTR + i;
-        const int nf = q / G::B_FRAGS_PER_NF, sub = q % G::B_FRAGS_PER_NF;
-        const uint8_t* src = wexp + ((int64_t)s * (p.N / 32) + nb * 8 + nf) * (C::B_ROW * 32) + sub * 1024 + lane * 16;
+    // Copy instruction c (0 <= c < CPS) of stage s into LDS stage buffer st:
+    // A rows, then weight fragments, then block scales.
+    auto copy = [&](auto ci, int s, uint8_t* st) {
+      constexpr int c = decltype(ci)::value;
+      constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
+      if constexpr (c < G::A_INSTR) {
+        g2lds16(p.a + a_off[c] + s * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
+      } else if constexpr (c < SC) {
+        // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
+        // global [layout stage][32-row block][KS_PER_L K-steps][FRAG]
+        const int q = w * G::B_INSTR + (c - G::A_INSTR);
+        const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
+        const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
+        const int kg = s * C::STEPS + ksl;
+        const uint8_t* src = wexp + ((int64_t)(kg / C::KS_PER_L) * (p.N / 32) + nb * 8 + nf) * (C::KS_PER_L * C::FRAG) +
+                             (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
         g2lds16(src, st + G::A_STAGE + q * 1024);
-      }
-      if constexpr (C::SCALED && !C::NV) {
+      } else if constexpr (!C::NV && c == SC) {
         // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
-        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 4,
+        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + (s / G::SPL) * 4,
                                          (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
+      } else if constexpr (!C::NV) {
         // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
-        const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
+        const uint8_t* src = wsf + ((int64_t)(s / G::SPL) * (p.N / 32) + nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
         g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
-      } else if constexpr (C::NV) {
-        // A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM), as two
-        // halves of 4 (64-K group 0, group 1)
-        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8,
-                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8 + 4,
-                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 + w * 256), 4, 0, 0);
-        // B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
+      } else if constexpr (c < SC + 2) {
+        // NVFP4 A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM),
+        // as two halves of 4 (64-K group 0, group 1)
+        constexpr int h = c - SC;
+        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8 + 4 * h,
+                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 * h + w * 256), 4, 0, 0);
+      } else {
+        // NVFP4 B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
         const int byte = (lane * 16) % (TN * 256);
         const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
         g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
       }
+    };
+    // copies [LO, HI) of stage s into buffer buf
+    auto issue = [&](auto lo, auto hi, int s, int buf) {
+      uint8_t* st = smem + buf * G::STAGE;
+      static_for<decltype(lo)::value, decltype(hi)::value>([&](auto ci) { copy(ci, s, st); });
     };
 
     f32x16 acc[TM][TN];
@@ -296,27 +336,38 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Stage s lives in LDS buffer s & 1.  Stage s+1's copy is issued while
-    // stage s computes; each stage's wait + barrier sits just before its last
-    // K-step, so the next stage's first fragments are read while the last
-    // K-step's MFMAs run and no LDS latency follows the barrier.  Copies are
-    // issued unconditionally (stage indices clamped to the last stage, an
-    // in-bounds re-copy into the idle buffer) so they share a scheduling
-    // region with the MFMAs; the next tile drains them before reusing LDS.
-    auto read_scales = [&](const uint8_t* st, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN]) {
+    // Stages rotate through NBUF LDS buffers; while stage s computes, the
+    // copies of stages s+1 .. s+NBUF-1 are in flight.  Each stage's wait +
+    // barrier sits just before its last K-step, so the next stage's first
+    // fragments are read while the last K-step's MFMAs run and no LDS latency
+    // follows the barrier.  Copies are issued unconditionally (stage indices
+    // clamped to the last stage, an in-bounds re-copy into a buffer that is
+    // not read again) so they share a scheduling region with the MFMAs; the
+    // next tile drains them before reusing LDS.
+    // Block scales of a stage (in buffer st) of parity PAR.  MX: the one
+    // UE8M0 byte each lane hands its scaled MFMA (a 64-K stage uses half of
+    // its 128-K layout stage's scales; lane group g takes A block 2*PAR + g),
+    // read as bytes so no VALU work waits on the LDS read.  NVFP4: dwords of
+    // 4 E4M3 scales.
+    auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN]) {
+      constexpr int PAR = decltype(parc)::value;
       if constexpr (C::SCALED) {
         const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
         const uint8_t* Bsf = Asf + G::A_SF_STAGE;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           const int r = wm * TM * 32 + tm * 32 + l32;
-          sa[tm] = *(const uint32_t*)(Asf + r * 4);
-          if constexpr (C::NV) sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
+          if constexpr (C::NV) {
+            sa[tm] = *(const uint32_t*)(Asf + r * 4);
+            sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
+          } else {
+            sa[tm] = Asf[r * 4 + 2 * PAR + g];
+          }
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           if constexpr (C::NV) sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
-          else sb[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
+          else sb[tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + PAR];
         }
       }
     };
@@ -357,10 +408,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
             if constexpr (FMT == F_BF16) {
               acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
             } else {
-              const int sav = (sa[tm] >> (8 * (ks * 2 + g))) & 0xFF;
-              const int sbv = (sb[tn] >> (8 * ks)) & 0xFF;
+              static_assert(C::STEPS == 1, "MX stages hold one scaled K-step");
               acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, sav, 0, sbv);
+                  af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[tm], 0, (int)sb[tn]);
             }
           }
         }
@@ -377,37 +427,67 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[e];
       }
     }
-    issue(0, 0);
-    wait_vmcnt0();
-    __syncthreads();
-    issue(nstages > 1 ? 1 : 0, 1);
+    // prologue: stages 0 .. NBUF-2 into buffers 0 .. NBUF-2 (indices clamped)
+#pragma unroll
+    for (int i = 0; i + 1 < C::NBUF; ++i) issue(IC<0>{}, IC<G::CPS>{}, i < nstages ? i : nstages - 1, i);
+    wait_vmcnt<(C::NBUF - 2) * G::CPS>();
+    lds_barrier();
     FA af[2][TM];
     FB bfr[2][TN];
     uint32_t sa4[SA_N] = {}, sb2[TN] = {}, sa4n[SA_N] = {}, sb2n[TN] = {};
-    read_scales(smem, sa4, sb2);
+    read_scales(smem, IC<0>{}, sa4, sb2);
     load_frags<FMT, TM, TN>(smem, smem + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
-    for (int s = 0; s < nstages; ++s) {
-      const uint8_t* st = smem + (s & 1) * G::STAGE;
-#pragma unroll
-      for (int ks = 0; ks + 1 < C::STEPS; ++ks) {
-        load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-        mfmas(ks, af[ks & 1], bfr[ks & 1], sa4, sb2);
-        interleave_hint<0, READS, TM * TN * (C::NV ? 4 : 1)>();
-      }
-      // stage boundary: stage s+1 has landed and every wave is done reading
-      // stage s, whose buffer then takes stage s+2
-      wait_vmcnt0();
-      __syncthreads();
-      const uint8_t* nx = smem + ((s + 1) & 1) * G::STAGE;
-      read_scales(nx, sa4n, sb2n);
-      load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
-      issue(s + 2 < nstages ? s + 2 : nstages - 1, s & 1);
-      mfmas(C::STEPS - 1, af[(C::STEPS - 1) & 1], bfr[(C::STEPS - 1) & 1], sa4, sb2);
-      boundary_hint<READS + (C::SCALED ? SA_N + TN : 0), TM * TN * (C::NV ? 4 : 1), G::A_INSTR + G::B_INSTR + (C::SCALED ? (C::NV ? 3 : 2) : 0)>();
+    constexpr int MF = TM * TN * (C::NV ? 4 : 1);   // MFMAs per K-step
+    int cur = 0;  // buffer of stage s
+    // One stage.  RB: register set holding the stage's first K-step
+    // fragments (K-step ks uses set (RB + ks) & 1; the next stage's first
+    // fragments go to set (RB + STEPS) & 1).
+    auto stage = [&](auto rbc, int s) {
+      constexpr int RB = decltype(rbc)::value;
+      const uint8_t* st = smem + cur * G::STAGE;
+      // stage s + NBUF - 1 goes into the buffer stage s - 1 left, its copies
+      // spread over the K-steps of stage s
+      const int fill = cur == 0 ? C::NBUF - 1 : cur - 1;
+      const int sf = s + C::NBUF - 1 < nstages ? s + C::NBUF - 1 : nstages - 1;
+      static_for<0, C::STEPS - 1>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        constexpr int lo = ks * G::CPS / C::STEPS, hi = (ks + 1) * G::CPS / C::STEPS;
+        constexpr int r0 = (RB + ks) & 1, r1 = (RB + ks + 1) & 1;
+        load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
+        issue(IC<lo>{}, IC<hi>{}, sf, fill);
+        mfmas(ks, af[r0], bfr[r0], sa4, sb2);
+        boundary_hint<READS, MF, hi - lo>();
+      });
+      // stage boundary: stage s+1 has landed (this wave's copies of stages
+      // s+2 .. s+NBUF-2 and the first part of s+NBUF-1 may still be in
+      // flight) and every wave is done reading stage s
+      constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies of s+NBUF-1 issued so far
+      constexpr int rl = (RB + C::STEPS - 1) & 1, rn = (RB + C::STEPS) & 1;
+      wait_vmcnt<(C::NBUF - 3) * G::CPS + LAST>();
+      lds_barrier();
+      const int nxt = cur + 1 == C::NBUF ? 0 : cur + 1;
+      const uint8_t* nx = smem + nxt * G::STAGE;
+      // with one K-step per stage, RB is the stage's parity
+      read_scales(nx, IC<(RB + 1) & 1>{}, sa4n, sb2n);
+      load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
+      issue(IC<LAST>{}, IC<G::CPS>{}, sf, fill);
+      mfmas(C::STEPS - 1, af[rl], bfr[rl], sa4, sb2);
+      boundary_hint<READS + (C::SCALED ? SA_N + TN : 0), MF, G::CPS - LAST>();
 #pragma unroll
       for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
+      cur = nxt;
+    };
+    if constexpr (C::STEPS % 2 == 0) {
+      for (int s = 0; s < nstages; ++s) stage(IC<0>{}, s);
+    } else {
+      int s = 0;
+      for (; s + 1 < nstages; s += 2) {
+        stage(IC<0>{}, s);
+        stage(IC<1>{}, s + 1);
+      }
+      if (s < nstages) stage(IC<0>{}, s);
     }
 
     // ---- epilogue.  Accumulator element v of lane l is row

@@ -69,11 +69,13 @@ const char* moe_status_string(int status);
 
 /* BLOCK_M the expert groups are padded to for `num_tokens` tokens
  * (get_block_m on the DeepGEMM MegaMoE page names the inputs but prints no
- * formula).  This library's rule: the smallest of 32, 64, 128, 256 that is at
- * least the expected rows per expert, num_tokens * (top_k + num_shared) /
- * (num_local_experts + num_shared), else 256.  Returns BLOCK_M > 0, or
- * MOE_E_INVALID for num_tokens < 0, top_k < 1, num_local_experts < 1 or
- * num_shared < 0.  Host-only; enqueues nothing. */
+ * formula).  This library's rule: with routed group sizes near-Poisson
+ * with mean num_tokens * top_k / num_local_experts and shared groups of
+ * num_tokens rows, the candidate of 32, 64, 128, 256 (NVFP4: up to 128)
+ * whose expected padded row count, divided by the tile's relative MFMA
+ * efficiency (0.35, 0.55, 0.85, 1.0), is smallest.  Returns BLOCK_M > 0, or MOE_E_INVALID for
+ * num_tokens < 0, top_k < 1, num_local_experts < 1, num_shared < 0 or an
+ * unknown format.  Host-only; enqueues nothing. */
 int moe_get_block_m(int num_tokens, int num_local_experts, int num_shared,
                     int top_k, moe_format_t fmt);
 
@@ -147,7 +149,7 @@ int moe_quantize_x(moe_format_t fmt, int num_tokens, int hidden, const void* x,
  * The buffers must hold the maximum sizes (sorted_slot: S + E'(block_m - 1),
  * tile_expert: that / block_m).  This is the kernel moe_forward runs; it is
  * exported so the metadata can be checked on its own.  topk_ids: int32
- * [T, top_k] (device).  block_m in {32, 64, 128, 256}; E' <= 1024. */
+ * [T, top_k] (device).  block_m in {32, 64, 128, 256}; E' = num_local_experts + num_shared <= 1000. */
 int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start,
                  int num_local_experts, int block_m, const int32_t* topk_ids,
                  int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
