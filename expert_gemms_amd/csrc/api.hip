@@ -133,13 +133,13 @@ double expected_padded(double m, int bm) {
 // BLOCK_M from the expected group sizes (routed experts T*k/n_loc rows,
 // shared experts T): each candidate's expected padded row count is weighed by
 // the tile's relative MFMA efficiency (smaller tiles re-read more operand
-// bytes per FLOP); the cheapest wins.  NVFP4 stops at 128 (its 256-row tile
-// runs out of registers).
+// bytes per FLOP); the cheapest wins.  The block-scaled formats stop at 128
+// (their 256-row tiles run out of registers).
 int block_m_rule(int T, int n_loc, int n_sh, int k, int fmt) {
   const double routed = (double)T * k / n_loc;
   const int cand[4] = {32, 64, 128, 256};
   const double eff[4] = {0.35, 0.55, 0.85, 1.0};
-  const int nc = fmt == MOE_FMT_NVFP4 ? 3 : 4;
+  const int nc = fmt == MOE_FMT_BF16 ? 4 : 3;
   int best = 32;
   double best_cost = -1.0;
   for (int i = 0; i < nc; ++i) {

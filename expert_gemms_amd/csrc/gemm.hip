@@ -94,8 +94,13 @@ struct TileGeom {
   static constexpr int A_SF_STAGE = C::SCALED ? (C::NV ? 2 : 1) * 4 * 256 : 0;
   static constexpr int B_SF_STAGE = C::SCALED ? 4 * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
-  static constexpr int ROWS_OFF = C::NBUF * STAGE;      // per-row epilogue scales (NVFP4)
-  static constexpr int LDS = C::NBUF * STAGE + (C::NV ? 1024 : 0);
+  // LDS stage buffers: the format's ring depth for the large (MFMA-bound)
+  // tiles; as many as fit, up to 8, for the small tiles of weight-streaming
+  // launches, whose stages are short and need more copies in flight.
+  static constexpr int NBUF_FIT = (160 * 1024 - (C::NV ? 1024 : 0)) / STAGE;
+  static constexpr int NBUF = BM >= 128 ? C::NBUF : (NBUF_FIT < 8 ? NBUF_FIT : 8);
+  static constexpr int ROWS_OFF = NBUF * STAGE;      // per-row epilogue scales (NVFP4)
+  static constexpr int LDS = NBUF * STAGE + (C::NV ? 1024 : 0);
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
   static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // per wave
   static constexpr int A_RPI = 1024 / C::A_ROW;         // A rows per copy instruction
@@ -103,8 +108,9 @@ struct TileGeom {
   static constexpr int B_FRAGS_PER_NF = C::B_ROW * 32 / 1024;   // 1 KiB copies per 32-row block
   // copy instructions per wave per stage (the in-flight count of the ring)
   static constexpr int CPS = A_INSTR + B_INSTR + (C::SCALED ? (C::NV ? 3 : 2) : 0);
+  static_assert((NBUF - 2) * CPS < 64, "vmcnt holds 6 bits");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small");
-  static_assert(C::NBUF >= 3, "the copies of stage s + NBUF - 1 are spread over stage s");
+  static_assert(NBUF >= 3, "the copies of stage s + NBUF - 1 are spread over stage s");
   static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
   // kernel stages per 128-K stage of the block-scale layouts
   static constexpr int SPL = 128 / C::KSTAGE;
@@ -236,10 +242,18 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
 
-  for (int base = 0; base < total; base += gridDim.x) {
-    const int u = base + xcd * per_xcd + xj;
-    if (u >= total) continue;
-    // ---- tile -> (expert, n block, m block)
+  // One tile: an expert, a 256-column block and a BLOCK_M-row block, with the
+  // per-lane source offsets of its A rows.
+  struct TileCtx {
+    int e, nb, m0;
+    int64_t a_off[G::A_INSTR];
+    int64_t asf_off;
+    const uint8_t* wexp;
+    const uint8_t* wsf;
+  };
+  auto make_tile = [&](int u) __attribute__((always_inline)) -> TileCtx {
+    TileCtx t;
+    // tile -> (expert, n block, m block)
     int lo = 0, hi = p.num_experts - 1;
     while (lo < hi) {  // largest e with tile_start(e) <= u
       int mid = (lo + hi + 1) >> 1;
@@ -249,86 +263,204 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
     const int mb0 = p.offsets[e] / BM;
     const int mcount = p.offsets[e + 1] / BM - mb0;
     const int local = u - mb0 * NB;
-    const int nb = local / mcount;
-    const int m0 = (mb0 + local % mcount) * BM;
-
-    // ---- per-lane A row offsets for the LDS-DMA copies: lane l of copy i
-    // fills LDS row r = A_RPI * (copy index) + l / A_CPR, physical chunk
-    // l % A_CPR (rows wrap modulo BM when a wave has more lanes than rows)
-    int64_t a_off[G::A_INSTR];
+    t.e = e;
+    t.nb = local / mcount;
+    t.m0 = (mb0 + local % mcount) * BM;
+    // per-lane A row offsets for the LDS-DMA copies: lane l of copy i fills
+    // LDS row r = A_RPI * (copy index) + l / A_CPR, physical chunk l % A_CPR
+    // (rows wrap modulo BM when a wave has more lanes than rows)
 #pragma unroll
     for (int i = 0; i < G::A_INSTR; ++i) {
       const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
       const int r = rl % BM;
       int64_t row;
       if (LAYER == 1) {
-        const int s = p.sorted_slot[m0 + r];
-        row = s >= 0 ? s / p.kk : 0;
+        const int sl = p.sorted_slot[t.m0 + r];
+        row = sl >= 0 ? sl / p.kk : 0;
       } else {
-        row = m0 + r;
+        row = t.m0 + r;
       }
-      a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
+      t.a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
     }
-    int64_t asf_off = 0;
+    t.asf_off = 0;
     if constexpr (C::SCALED) {
       const int r = (w * 64 + lane) % BM;
       int64_t row;
       if (LAYER == 1) {
-        const int s = p.sorted_slot[m0 + r];
-        row = s >= 0 ? s / p.kk : 0;
+        const int sl = p.sorted_slot[t.m0 + r];
+        row = sl >= 0 ? sl / p.kk : 0;
       } else {
-        row = m0 + r;
+        row = t.m0 + r;
       }
-      asf_off = row * p.a_sf_ld;
+      t.asf_off = row * p.a_sf_ld;
     }
-    const uint8_t* wexp = p.w + (int64_t)e * p.w_expert_bytes;
-    const uint8_t* wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
+    t.wexp = p.w + (int64_t)e * p.w_expert_bytes;
+    t.wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
+    return t;
+  };
 
-    // Copy instruction c (0 <= c < CPS) of stage s into LDS stage buffer st:
-    // A rows, then weight fragments, then block scales.
-    auto copy = [&](auto ci, int s, uint8_t* st) {
-      constexpr int c = decltype(ci)::value;
-      constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
-      if constexpr (c < G::A_INSTR) {
-        g2lds16(p.a + a_off[c] + s * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
-      } else if constexpr (c < SC) {
-        // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
-        // global [layout stage][32-row block][KS_PER_L K-steps][FRAG]
-        const int q = w * G::B_INSTR + (c - G::A_INSTR);
-        const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
-        const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
-        const int kg = s * C::STEPS + ksl;
-        const uint8_t* src = wexp + ((int64_t)(kg / C::KS_PER_L) * (p.N / 32) + nb * 8 + nf) * (C::KS_PER_L * C::FRAG) +
-                             (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
-        g2lds16(src, st + G::A_STAGE + q * 1024);
-      } else if constexpr (!C::NV && c == SC) {
-        // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
-        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + (s / G::SPL) * 4,
-                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
-      } else if constexpr (!C::NV) {
-        // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
-        const uint8_t* src = wsf + ((int64_t)(s / G::SPL) * (p.N / 32) + nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
-        g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
-      } else if constexpr (c < SC + 2) {
-        // NVFP4 A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM),
-        // as two halves of 4 (64-K group 0, group 1)
-        constexpr int h = c - SC;
-        __builtin_amdgcn_global_load_lds(p.a_sf + asf_off + s * 8 + 4 * h,
-                                         (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 * h + w * 256), 4, 0, 0);
-      } else {
-        // NVFP4 B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
-        const int byte = (lane * 16) % (TN * 256);
-        const uint8_t* src = wsf + ((int64_t)s * (p.N / 32) + nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
-        g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
+  // Copy instruction c (0 <= c < CPS) of stage s into LDS stage buffer st:
+  // A rows, then weight fragments, then block scales.
+  auto copy = [&](auto ci, const TileCtx t, int s, uint8_t* st) __attribute__((always_inline)) {
+    constexpr int c = decltype(ci)::value;
+    constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
+    if constexpr (c < G::A_INSTR) {
+      g2lds16(p.a + t.a_off[c] + s * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
+    } else if constexpr (c < SC) {
+      // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
+      // global [layout stage][32-row block][KS_PER_L K-steps][FRAG]
+      const int q = w * G::B_INSTR + (c - G::A_INSTR);
+      const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
+      const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
+      const int kg = s * C::STEPS + ksl;
+      const uint8_t* src = t.wexp + ((int64_t)(kg / C::KS_PER_L) * (p.N / 32) + t.nb * 8 + nf) * (C::KS_PER_L * C::FRAG) +
+                           (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
+      g2lds16(src, st + G::A_STAGE + q * 1024);
+    } else if constexpr (!C::NV && c == SC) {
+      // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
+      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + (s / G::SPL) * 4,
+                                       (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
+    } else if constexpr (!C::NV) {
+      // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
+      const uint8_t* src = t.wsf + ((int64_t)(s / G::SPL) * (p.N / 32) + t.nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
+      g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
+    } else if constexpr (c < SC + 2) {
+      // NVFP4 A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM),
+      // as two halves of 4 (64-K group 0, group 1)
+      constexpr int h = c - SC;
+      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + s * 8 + 4 * h,
+                                       (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 * h + w * 256), 4, 0, 0);
+    } else {
+      // NVFP4 B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
+      const int byte = (lane * 16) % (TN * 256);
+      const uint8_t* src = t.wsf + ((int64_t)s * (p.N / 32) + t.nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
+      g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
+    }
+  };
+  // copies [LO, HI) of stage s of tile t into buffer buf
+  auto issue = [&](auto lo, auto hi, const TileCtx t, int s, int buf) __attribute__((always_inline)) {
+    uint8_t* st = smem + buf * G::STAGE;
+    static_for<decltype(lo)::value, decltype(hi)::value>([&](auto ci) __attribute__((always_inline)) { copy(ci, t, s, st); });
+  };
+
+  f32x16 acc[TM][TN];   // the tile's accumulators (AGPRs)
+  // Block scales of a stage (in buffer st) of parity PAR.  MX: the one
+  // UE8M0 byte each lane hands its scaled MFMA (a 64-K stage uses half of
+  // its 128-K layout stage's scales; lane group g takes A block 2*PAR + g),
+  // read as bytes so no VALU work waits on the LDS read.  NVFP4: dwords of
+  // 4 E4M3 scales.
+  auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN])
+      __attribute__((always_inline)) {
+    constexpr int PAR = decltype(parc)::value;
+    if constexpr (C::SCALED) {
+      const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
+      const uint8_t* Bsf = Asf + G::A_SF_STAGE;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int r = wm * TM * 32 + tm * 32 + l32;
+        if constexpr (C::NV) {
+          sa[tm] = *(const uint32_t*)(Asf + r * 4);
+          sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
+        } else {
+          sa[tm] = Asf[r * 4 + 2 * PAR + g];
+        }
       }
-    };
-    // copies [LO, HI) of stage s into buffer buf
-    auto issue = [&](auto lo, auto hi, int s, int buf) {
-      uint8_t* st = smem + buf * G::STAGE;
-      static_for<decltype(lo)::value, decltype(hi)::value>([&](auto ci) { copy(ci, s, st); });
-    };
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (C::NV) sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
+        else sb[tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + PAR];
+      }
+    }
+  };
+  auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
+                   const uint32_t (&sb)[TN]) __attribute__((always_inline)) {
+    if constexpr (C::NV) {
+      // 64-K group ks: four 16-wide K-steps; sub-step j takes the lane's
+      // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
+      // group: byte 2g + j/2 of the row's A-scale dword, byte 2ks + j/2 of
+      // the lane's B-scale dword
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
+        NvScale ssa[TM], ssb[TN];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * (2 * g + h))) & 0xFF);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) ssb[tn] = nv_scale((sb[tn] >> (8 * (2 * ks + h))) & 0xFF);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * h + jj;
+          f16x8 a8[TM], b8[TN];
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) a8[tm] = nvfp4_to_f16x8(af[tm][j], ssa[tm]);
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) b8[tn] = nvfp4_to_f16x8(bf[tn][j], ssb[tn]);
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[tm], b8[tn], acc[tm][tn], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          if constexpr (FMT == F_BF16) {
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+          } else {
+            static_assert(C::STEPS == 1, "MX stages hold one scaled K-step");
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[tm], 0, (int)sb[tn]);
+          }
+        }
+      }
+    }
+  };
 
-    f32x16 acc[TM][TN];
+  // Stages rotate through NBUF LDS buffers; while stage s computes, the
+  // copies of stages s+1 .. s+NBUF-1 are in flight, those of stage
+  // s+NBUF-1 spread over stage s's K-steps into the buffer stage s-1 left.
+  // Each stage's wait + barrier sits just before its last K-step, so the
+  // next stage's first fragments are read while the last K-step's MFMAs
+  // run.  The last NBUF-1 stages of a tile issue the first stages of the
+  // workgroup's next tile (when K has at least NBUF-1 stages), so the next
+  // tile starts without a pipeline fill and its copies overlap this tile's
+  // epilogue; with no next tile, the copies re-copy the last stage into a
+  // buffer that is not read again (stage indices clamped), which keeps the
+  // copy count per stage fixed for the vmcnt bookkeeping.
+  const bool chain = nstages >= G::NBUF - 1;
+  const int u0 = xcd * per_xcd + xj;
+  TileCtx ta, tb;
+  int cur = 0;           // LDS buffer of the current stage
+  bool primed = false;   // the current tile's first NBUF-1 stages are issued
+  if (u0 < total) ta = make_tile(u0);
+  for (int u = u0; u < total; u += gridDim.x) {
+    const bool has_next = u + (int)gridDim.x < total;
+    if (has_next) tb = make_tile(u + gridDim.x);
+    const bool chain_next = chain && has_next;
+    lds_barrier();        // every wave is done with the previous tile's LDS
+    // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
+    // (read after the K loop's barriers)
+    if constexpr (C::NV && LAYER == 1) {
+      if (tid < BM) {
+        const int sl = p.sorted_slot[ta.m0 + tid];
+        ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[ta.e];
+      }
+    }
+    if (!primed) {
+      // a tile the previous one could not prefetch: drain that tile's
+      // clamped re-copies, then issue stages 0 .. NBUF-2
+      wait_vmcnt0();
+#pragma unroll
+      for (int i = 0; i + 1 < G::NBUF; ++i) {
+        const int bi = cur + i < G::NBUF ? cur + i : cur + i - G::NBUF;
+        issue(IC<0>{}, IC<G::CPS>{}, ta, i < nstages ? i : nstages - 1, bi);
+      }
+    }
+    wait_vmcnt<(G::NBUF - 2) * G::CPS>();
+    lds_barrier();
+
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -336,159 +468,85 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Stages rotate through NBUF LDS buffers; while stage s computes, the
-    // copies of stages s+1 .. s+NBUF-1 are in flight.  Each stage's wait +
-    // barrier sits just before its last K-step, so the next stage's first
-    // fragments are read while the last K-step's MFMAs run and no LDS latency
-    // follows the barrier.  Copies are issued unconditionally (stage indices
-    // clamped to the last stage, an in-bounds re-copy into a buffer that is
-    // not read again) so they share a scheduling region with the MFMAs; the
-    // next tile drains them before reusing LDS.
-    // Block scales of a stage (in buffer st) of parity PAR.  MX: the one
-    // UE8M0 byte each lane hands its scaled MFMA (a 64-K stage uses half of
-    // its 128-K layout stage's scales; lane group g takes A block 2*PAR + g),
-    // read as bytes so no VALU work waits on the LDS read.  NVFP4: dwords of
-    // 4 E4M3 scales.
-    auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN]) {
-      constexpr int PAR = decltype(parc)::value;
-      if constexpr (C::SCALED) {
-        const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
-        const uint8_t* Bsf = Asf + G::A_SF_STAGE;
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-          const int r = wm * TM * 32 + tm * 32 + l32;
-          if constexpr (C::NV) {
-            sa[tm] = *(const uint32_t*)(Asf + r * 4);
-            sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
-          } else {
-            sa[tm] = Asf[r * 4 + 2 * PAR + g];
-          }
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          if constexpr (C::NV) sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
-          else sb[tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + PAR];
-        }
-      }
-    };
-    auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
-                     const uint32_t (&sb)[TN]) {
-      if constexpr (C::NV) {
-        // 64-K group ks: four 16-wide K-steps; sub-step j takes the lane's
-        // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
-        // group: byte 2g + j/2 of the row's A-scale dword, byte 2ks + j/2 of
-        // the lane's B-scale dword
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
-          NvScale ssa[TM], ssb[TN];
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * (2 * g + h))) & 0xFF);
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) ssb[tn] = nv_scale((sb[tn] >> (8 * (2 * ks + h))) & 0xFF);
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * h + jj;
-            f16x8 a8[TM], b8[TN];
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) a8[tm] = nvfp4_to_f16x8(af[tm][j], ssa[tm]);
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) b8[tn] = nvfp4_to_f16x8(bf[tn][j], ssb[tn]);
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-              for (int tn = 0; tn < TN; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[tm], b8[tn], acc[tm][tn], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            if constexpr (FMT == F_BF16) {
-              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
-            } else {
-              static_assert(C::STEPS == 1, "MX stages hold one scaled K-step");
-              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[tm], 0, (int)sb[tn]);
-            }
-          }
-        }
-      }
-    };
-
-    wait_vmcnt0();
-    __syncthreads();          // the previous tile's copies and reads are done
-    // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
-    // (read after the K loop's barriers)
-    if constexpr (C::NV && LAYER == 1) {
-      if (tid < BM) {
-        const int sl = p.sorted_slot[m0 + tid];
-        ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[e];
-      }
-    }
-    // prologue: stages 0 .. NBUF-2 into buffers 0 .. NBUF-2 (indices clamped)
-#pragma unroll
-    for (int i = 0; i + 1 < C::NBUF; ++i) issue(IC<0>{}, IC<G::CPS>{}, i < nstages ? i : nstages - 1, i);
-    wait_vmcnt<(C::NBUF - 2) * G::CPS>();
-    lds_barrier();
     FA af[2][TM];
     FB bfr[2][TN];
     uint32_t sa4[SA_N] = {}, sb2[TN] = {}, sa4n[SA_N] = {}, sb2n[TN] = {};
-    read_scales(smem, IC<0>{}, sa4, sb2);
-    load_frags<FMT, TM, TN>(smem, smem + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
+    {
+      const uint8_t* st0 = smem + cur * G::STAGE;
+      read_scales(st0, IC<0>{}, sa4, sb2);
+      load_frags<FMT, TM, TN>(st0, st0 + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
+    }
     constexpr int MF = TM * TN * (C::NV ? 4 : 1);   // MFMAs per K-step
-    int cur = 0;  // buffer of stage s
     // One stage.  RB: register set holding the stage's first K-step
     // fragments (K-step ks uses set (RB + ks) & 1; the next stage's first
-    // fragments go to set (RB + STEPS) & 1).
-    auto stage = [&](auto rbc, int s) {
+    // fragments go to set (RB + STEPS) & 1).  LASTC: the tile's last stage
+    // (no next stage to wait for or read).
+    auto stage = [&](auto rbc, auto lastc, int s) __attribute__((always_inline)) {
       constexpr int RB = decltype(rbc)::value;
+      constexpr bool LASTS = decltype(lastc)::value;
       const uint8_t* st = smem + cur * G::STAGE;
-      // stage s + NBUF - 1 goes into the buffer stage s - 1 left, its copies
-      // spread over the K-steps of stage s
-      const int fill = cur == 0 ? C::NBUF - 1 : cur - 1;
-      const int sf = s + C::NBUF - 1 < nstages ? s + C::NBUF - 1 : nstages - 1;
-      static_for<0, C::STEPS - 1>([&](auto kc) {
+      // stage s + NBUF - 1 (of this tile, else of the next) goes into the
+      // buffer stage s - 1 left, its copies spread over stage s's K-steps
+      const int fill = cur == 0 ? G::NBUF - 1 : cur - 1;
+      const int sf = s + G::NBUF - 1;
+      const bool own = sf < nstages;
+      const int js = own ? sf : (chain_next ? sf - nstages : nstages - 1);
+      const bool from_next = !own && chain_next;
+      // copy source (a uniform branch: selects would make the tiles addressable)
+      TileCtx tf = ta;
+      if (from_next) tf = tb;
+      static_for<0, C::STEPS - 1>([&](auto kc) __attribute__((always_inline)) {
         constexpr int ks = decltype(kc)::value;
         constexpr int lo = ks * G::CPS / C::STEPS, hi = (ks + 1) * G::CPS / C::STEPS;
         constexpr int r0 = (RB + ks) & 1, r1 = (RB + ks + 1) & 1;
         load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
-        issue(IC<lo>{}, IC<hi>{}, sf, fill);
+        issue(IC<lo>{}, IC<hi>{}, tf, js, fill);
         mfmas(ks, af[r0], bfr[r0], sa4, sb2);
         boundary_hint<READS, MF, hi - lo>();
       });
-      // stage boundary: stage s+1 has landed (this wave's copies of stages
-      // s+2 .. s+NBUF-2 and the first part of s+NBUF-1 may still be in
-      // flight) and every wave is done reading stage s
       constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies of s+NBUF-1 issued so far
       constexpr int rl = (RB + C::STEPS - 1) & 1, rn = (RB + C::STEPS) & 1;
-      wait_vmcnt<(C::NBUF - 3) * G::CPS + LAST>();
-      lds_barrier();
-      const int nxt = cur + 1 == C::NBUF ? 0 : cur + 1;
-      const uint8_t* nx = smem + nxt * G::STAGE;
-      // with one K-step per stage, RB is the stage's parity
-      read_scales(nx, IC<(RB + 1) & 1>{}, sa4n, sb2n);
-      load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
-      issue(IC<LAST>{}, IC<G::CPS>{}, sf, fill);
+      const int nxt = cur + 1 == G::NBUF ? 0 : cur + 1;
+      if constexpr (!LASTS) {
+        // stage boundary: stage s+1 has landed (this wave's copies of
+        // stages s+2 .. s+NBUF-2 and the first part of s+NBUF-1 may still
+        // be in flight) and every wave is done reading stage s
+        wait_vmcnt<(G::NBUF - 3) * G::CPS + LAST>();
+        lds_barrier();
+        const uint8_t* nx = smem + nxt * G::STAGE;
+        // with one K-step per stage, RB is the stage's parity
+        read_scales(nx, IC<(RB + 1) & 1>{}, sa4n, sb2n);
+        load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
+      }
+      issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
       mfmas(C::STEPS - 1, af[rl], bfr[rl], sa4, sb2);
-      boundary_hint<READS + (C::SCALED ? SA_N + TN : 0), MF, G::CPS - LAST>();
+      boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + TN : 0), MF, G::CPS - LAST>();
+      if constexpr (!LASTS) {
 #pragma unroll
-      for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
+        for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
+        for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
+      }
       cur = nxt;
     };
     if constexpr (C::STEPS % 2 == 0) {
-      for (int s = 0; s < nstages; ++s) stage(IC<0>{}, s);
+      for (int s = 0; s + 1 < nstages; ++s) stage(IC<0>{}, std::false_type{}, s);
+      stage(IC<0>{}, std::true_type{}, nstages - 1);
     } else {
       int s = 0;
-      for (; s + 1 < nstages; s += 2) {
-        stage(IC<0>{}, s);
-        stage(IC<1>{}, s + 1);
+      for (; s + 2 < nstages; s += 2) {
+        stage(IC<0>{}, std::false_type{}, s);
+        stage(IC<1>{}, std::false_type{}, s + 1);
       }
-      if (s < nstages) stage(IC<0>{}, s);
+      if (s + 1 < nstages) {
+        stage(IC<0>{}, std::false_type{}, s);
+        stage(IC<1>{}, std::true_type{}, s + 1);
+      } else {
+        stage(IC<0>{}, std::true_type{}, s);
+      }
     }
+    primed = chain_next;
+    const int e = ta.e, nb = ta.nb, m0 = ta.m0;
 
     // ---- epilogue.  Accumulator element v of lane l is row
     // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32 of its 32x32 tile.
@@ -561,7 +619,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         }
       }
     }
+    if (has_next) ta = tb;
   }
+  wait_vmcnt0();   // no LDS-DMA copy outlives the workgroup
 }
 
 // ------------------------------------------------------------------ host side

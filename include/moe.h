@@ -71,7 +71,8 @@ const char* moe_status_string(int status);
  * (get_block_m on the DeepGEMM MegaMoE page names the inputs but prints no
  * formula).  This library's rule: with routed group sizes near-Poisson
  * with mean num_tokens * top_k / num_local_experts and shared groups of
- * num_tokens rows, the candidate of 32, 64, 128, 256 (NVFP4: up to 128)
+ * num_tokens rows, the candidate of 32, 64, 128, 256 (block-scaled formats:
+ * up to 128)
  * whose expected padded row count, divided by the tile's relative MFMA
  * efficiency (0.35, 0.55, 0.85, 1.0), is smallest.  Returns BLOCK_M > 0, or MOE_E_INVALID for
  * num_tokens < 0, top_k < 1, num_local_experts < 1, num_shared < 0 or an

@@ -59,16 +59,18 @@ def mx_scale_codes(amax, elem):
     return np.where(nz, c, 0).astype(np.uint8)
 
 
-def mx_quantize(v, elem):
+def mx_quantize(v, elem, codes=None):
     """float32 [..., K] -> (codes uint8 [..., K] (4-bit codes for E2M1,
-    unpacked), UE8M0 scales uint8 [..., K/32])."""
+    unpacked), UE8M0 scales uint8 [..., K/32]).  ``codes``: UE8M0 scales to
+    quantise the elements with instead of choosing them (a given decision)."""
     v = np.asarray(v, dtype=np.float32)
     K = v.shape[-1]
     if K % MX_GROUP:
         raise ValueError("K must be a multiple of 32")
     blk = v.reshape(v.shape[:-1] + (K // MX_GROUP, MX_GROUP)).astype(np.float64)
     amax = np.abs(blk).max(axis=-1)
-    c = mx_scale_codes(amax, elem)
+    c = mx_scale_codes(amax, elem) if codes is None else np.broadcast_to(
+        np.asarray(codes, dtype=np.uint8), amax.shape)
     # v * 2**(127 - c): exact (a power-of-two scaling) in float64.
     scaled = blk * np.ldexp(1.0, 127 - c.astype(np.int64))[..., None]
     enc = codecs.e4m3_encode if elem == "e4m3" else codecs.e2m1_encode
@@ -98,10 +100,11 @@ def nvfp4_global_scale(amax):
     return np.where(amax > 0, g, np.float32(1.0)).astype(np.float32)
 
 
-def nvfp4_quantize(v, g):
+def nvfp4_quantize(v, g, bs=None):
     """float32 [..., K] with global scale ``g`` (float32, broadcast over the
     leading axes, shape [...]) -> (E2M1 codes uint8 [..., K] unpacked,
-    E4M3 block-scale codes uint8 [..., K/16])."""
+    E4M3 block-scale codes uint8 [..., K/16]).  ``bs``: E4M3 block scales to
+    quantise the elements with instead of choosing them (a given decision)."""
     v = np.asarray(v, dtype=np.float32)
     K = v.shape[-1]
     if K % NV_GROUP:
@@ -112,7 +115,7 @@ def nvfp4_quantize(v, g):
     gb = np.broadcast_to(g[..., None], amax.shape).astype(np.float32)
     six_g = (np.float32(6.0) * gb).astype(np.float32)
     t = (amax / six_g).astype(np.float32)
-    bs = codecs.e4m3_encode(t)
+    bs = codecs.e4m3_encode(t) if bs is None else np.broadcast_to(np.asarray(bs, dtype=np.uint8), amax.shape)
     bsv = codecs.e4m3_decode(bs).astype(np.float32)          # exact in float32
     denom = (bsv * gb).astype(np.float32)
     safe = np.where(denom > 0, denom, np.float32(1.0))

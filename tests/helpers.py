@@ -8,7 +8,11 @@ oracle input is ever produced by the HIP path.
 import numpy as np
 import torch
 
+import itertools
+
 from oracle import codecs, quant
+from oracle.dispatch import slot_experts
+from oracle.moe import activation, dequant_weight, quantize_x
 from synth import gen_weight_f32, bf16_bits
 
 
@@ -72,3 +76,171 @@ def check_output(fmt, y_gpu, y_ref, rms=None):
     bound = TOL[fmt] * rms + bf16_half_ulp(y_ref)
     excess = float((err - bound).max()) if err.size else 0.0
     return float(err.max() / rms) if err.size and rms > 0 else 0.0, excess
+
+
+# --------------------------------------------------------------------------
+# L2-input quantisation decisions that sit on a boundary
+# --------------------------------------------------------------------------
+# The L2 input is quantised from the activations: its block scales and
+# element codes are integers decided by floating point.  Both sides decide in
+# float32 (the method's precision), but from activations summed in different
+# orders (MFMA float32 vs float64), so a value lying closer to a decision
+# boundary (an element's rounding midpoint, the amax where a block scale
+# changes) than the float32 evaluation error has two valid quantisations.
+# One flipped element moves its contribution by a whole code step, which for
+# a token with few L2 terms can exceed the bar.  For tokens over the bar, the
+# check recomputes that token with the other valid choice of each such
+# decision (every combination) and accepts it if one meets the bar; every
+# other token is compared as computed.  The evaluation error bound per
+# activation: 2^-19 of the sum of |products| behind g and u (float32
+# accumulation), carried through the activation, plus 2^-18 relative
+# (hardware exp and reciprocal).
+
+def _act_error(W13, xs, act):
+    """float64 activations a [I] of one slot and a bound on their float32
+    evaluation error."""
+    I = W13.shape[0] // 2
+    h = W13 @ xs
+    eh = np.ldexp(np.abs(W13) @ np.abs(xs), -19)
+    f = lambda g, u: activation(g, u, act.get("clamp"), act.get("alpha", 1.0), act.get("beta", 0.0))
+    g, u, eg, eu = h[:I], h[I:], eh[:I], eh[I:]
+    a = f(g, u)
+    da = np.max([np.abs(f(g + sg * eg, u + su * eu) - a) for sg in (-1, 1) for su in (-1, 1)], axis=0)
+    return a, da + np.ldexp(np.abs(a), -18)
+
+
+def decision_alternatives(fmt, a, da, g2=1.0):
+    """[(offset, change of the dequantised L2 input block)] for the
+    boundary decisions of one slot's L2 input (float64 activations ``a`` [I]
+    with evaluation error bound ``da``)."""
+    a32 = np.asarray(a, dtype=np.float64).astype(np.float32)
+    out = []
+    if fmt in ("mxfp8", "mxfp4"):
+        G = 32
+        for off in range(0, a32.size, G):
+            v = a32[off:off + G].astype(np.float64)
+            d = da[off:off + G]
+            i = int(np.abs(v).argmax())
+            amax = abs(v[i])
+            if amax == 0.0:
+                continue
+            q, c = quant.mx_quantize(v, "e4m3")
+            own = quant.mx_dequantize(q, c, "e4m3")
+            lo = int(quant.mx_scale_codes(amax - d[i], "e4m3"))
+            hi = int(quant.mx_scale_codes(amax + d[i], "e4m3"))
+            if lo != hi:                       # the block scale itself
+                other = hi if int(c[0]) == lo else lo
+                q2, c2 = quant.mx_quantize(v, "e4m3", codes=[other])
+                out.append((off, quant.mx_dequantize(q2, c2, "e4m3") - own))
+                continue
+            s = np.ldexp(1.0, 127 - int(c[0]))
+            sv, ds = v * s, d * s
+            qlo, qhi = codecs.e4m3_encode(sv - ds), codecs.e4m3_encode(sv + ds)
+            for k in np.nonzero(qlo != qhi)[0]:  # element rounding
+                other = qhi[k] if q[k] == qlo[k] else qlo[k]
+                delta = np.zeros(G)
+                delta[k] = (codecs.e4m3_decode(np.uint8(other)) - codecs.e4m3_decode(q[k])) / s
+                out.append((off, delta))
+    elif fmt == "nvfp4":
+        G = 16
+        g = np.float32(g2)
+        six_g = np.float32(np.float32(6.0) * g)
+        for off in range(0, a32.size, G):
+            v = a32[off:off + G]
+            d = da[off:off + G]
+            i = int(np.abs(v).argmax())
+            amax = float(abs(v[i]))
+            if amax == 0.0:
+                continue
+            q, bs = quant.nvfp4_quantize(v, g)
+            own = quant.nvfp4_dequantize(q, bs, g)
+            t, dt = amax / float(six_g), d[i] / float(six_g)
+            lo = int(codecs.e4m3_encode(np.float32(t - dt)))
+            hi = int(codecs.e4m3_encode(np.float32(t + dt)))
+            if lo != hi:
+                other = hi if int(bs[0]) == lo else lo
+                q2, bs2 = quant.nvfp4_quantize(v, g, bs=[other])
+                out.append((off, quant.nvfp4_dequantize(q2, bs2, g) - own))
+                continue
+            bsv = float(codecs.e4m3_decode(bs[0]))
+            if bsv == 0.0:
+                continue
+            r = 1.0 / (bsv * float(g))
+            pv, dp = v.astype(np.float64) * r, d * r
+            qlo, qhi = codecs.e2m1_encode(pv - dp), codecs.e2m1_encode(pv + dp)
+            for k in np.nonzero(qlo != qhi)[0]:
+                other = qhi[k] if q[k] == qlo[k] else qlo[k]
+                delta = np.zeros(G)
+                delta[k] = (codecs.e2m1_decode(np.uint8(other)) - codecs.e2m1_decode(q[k])) * bsv * float(g)
+                out.append((off, delta))
+    return out
+
+
+def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_start=0, num_local=None,
+                act=None, g2=1.0, tokens=None, max_decisions=12):
+    """check_output, plus the boundary-decision rule above for tokens over
+    the bar (every combination of a token's boundary decisions when there are
+    at most ``max_decisions``, else a greedy search).  ``tokens``: the token
+    index of each row (default: all rows in order).  Returns (max err / RMS as computed, worst excess after the rule,
+    number of tokens accepted under another valid decision)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    rel, excess = check_output(fmt, y_gpu, y_ref, rms=rms)
+    if excess <= 0 or fmt == "bf16":
+        return rel, excess, 0
+
+    def row_excess(yg, yr):
+        return float((np.abs(yg - yr) - (TOL[fmt] * rms + bf16_half_ulp(yr))).max())
+
+    tok = np.arange(y_ref.shape[0]) if tokens is None else np.asarray(tokens)
+    E_all = w["w13"].shape[0]
+    num_local = E_all - num_shared if num_local is None else num_local
+    ids = np.asarray(ids)
+    k = ids.shape[1]
+    act = dict(act or {})
+    cache = {}
+    worst, rescued = -np.inf, 0
+    for r in range(y_ref.shape[0]):
+        ex = row_excess(y_gpu[r], y_ref[r])
+        if ex <= 0:
+            worst = max(worst, ex)
+            continue
+        t = int(tok[r])
+        exp = slot_experts(ids[t:t + 1], num_shared, expert_start, num_local)[0]
+        xs = quantize_x(fmt, np.asarray(x_bits)[t:t + 1])[0]
+        deltas = []
+        for j, e in enumerate(exp):
+            if e < 0:
+                continue
+            if e not in cache:
+                cache[e] = (dequant_weight(fmt, w, "w13", e), dequant_weight(fmt, w, "w2", e))
+            W13, W2 = cache[e]
+            a, da = _act_error(W13, xs, act)
+            wj = float(wts[t, j]) if j < k else 1.0
+            for off, dv in decision_alternatives(fmt, a, da, g2):
+                deltas.append(wj * (W2[:, off:off + dv.size] @ dv))
+        best = ex
+        if 0 < len(deltas) <= max_decisions:
+            # every combination
+            for n in range(1, len(deltas) + 1):
+                for combo in itertools.combinations(deltas, n):
+                    best = min(best, row_excess(y_gpu[r], y_ref[r] + np.sum(combo, axis=0)))
+        elif deltas:
+            # too many to enumerate: add, one at a time, the decision that
+            # brings the oracle closest (2-norm) to the GPU row, while it helps
+            cur = y_ref[r].copy()
+            left = list(range(len(deltas)))
+            for _ in range(max_decisions):
+                if row_excess(y_gpu[r], cur) <= 0 or not left:
+                    break
+                norms = [np.linalg.norm(y_gpu[r] - cur - deltas[i]) for i in left]
+                i = int(np.argmin(norms))
+                if norms[i] >= np.linalg.norm(y_gpu[r] - cur):
+                    break
+                cur += deltas[left.pop(i)]
+            best = min(best, row_excess(y_gpu[r], cur))
+        if best <= 0:
+            rescued += 1
+        worst = max(worst, best)
+    return rel, worst, rescued

@@ -45,8 +45,9 @@ def test_block_m_rule():
     assert moe.moe_get_block_m(0, 8, 0, 2, "bf16") == 32
     # 256 expected rows per routed expert: half the groups spill past 256
     assert moe.moe_get_block_m(8192, 256, 1, 8, "mxfp8") == 128
-    assert moe.moe_get_block_m(16384, 64, 0, 6, "nvfp4") == 128     # NVFP4 stops at 128
-    assert moe.moe_get_block_m(16384, 64, 0, 6, "mxfp8") == 256
+    assert moe.moe_get_block_m(16384, 64, 0, 6, "nvfp4") == 128     # block-scaled formats stop at 128
+    assert moe.moe_get_block_m(16384, 64, 0, 6, "mxfp8") == 128
+    assert moe.moe_get_block_m(16384, 64, 0, 6, "bf16") == 256
     with pytest.raises(moe.MoEError):
         moe.moe_get_block_m(-1, 8, 0, 2, "bf16")
     with pytest.raises(moe.MoEError):

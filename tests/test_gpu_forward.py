@@ -2,7 +2,10 @@
 element, on seeded inputs that span several tiles and ragged tails.
 
 Bar (tests/helpers.check_output): |y_gpu - y_oracle| <= tol * RMS(y_oracle)
-+ half a BF16 ulp of y_oracle, tol = 1e-2 for BF16 and 3e-2 for MX/NVFP4.
++ half a BF16 ulp of y_oracle, tol = 1e-2 for BF16 and 3e-2 for MX/NVFP4; a
+token over it is accepted only if the oracle, recomputed with the other valid
+choice of its L2-input quantisation decisions that lie on a boundary, meets it
+(tests/helpers.check_layer).
 """
 
 import numpy as np
@@ -12,7 +15,7 @@ import torch
 from oracle.moe import moe_reference
 from synth import CONFIGS, MoEConfig, gen_routing, gen_x_bf16, gen_w2_input_scale, bf16_bits
 from tests.gpu_util import run_layer
-from tests.helpers import check_output, make_weights
+from tests.helpers import check_layer, check_output, make_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +26,21 @@ SMALL = {
                              routing="sigmoid_normal"),
     "mxfp4_small": MoEConfig("mxfp4_small", 13, "mxfp4", 37, 512, 384, 32, 8, routing="softmax_uniform"),
     "nvfp4_small": MoEConfig("nvfp4_small", 14, "nvfp4", 300, 512, 256, 16, 6, routing="zipf"),
+}
+
+# More tiles than the persistent grid has workgroups, so each workgroup runs
+# several tiles: with I = 1024 the next tile's first stages are prefetched
+# during the current tile; with a short I (L2 K shorter than the copy ring)
+# each tile fills the ring itself.  The short I is 256 for the MX formats:
+# with I = 128 an L2 output sums only 128 products of coarse E2M1 / E4M3
+# values, and one legitimate rounding-boundary flip of an MXFP8 L2 input
+# (fp32 accumulation order vs float64) already moves it by a few percent of
+# the output RMS.
+SHORT_I = {"bf16": 128, "mxfp8": 256, "mxfp4": 256, "nvfp4": 128}
+MULTI = {
+    f"{fmt}_multi_i{inter}": MoEConfig(f"{fmt}_multi_i{inter}", 20 + 2 * i + j, fmt, 4000, 1024, inter, 8, 2,
+                                       routing="softmax_uniform")
+    for i, fmt in enumerate(["bf16", "mxfp8", "mxfp4", "nvfp4"]) for j, inter in enumerate([1024, SHORT_I[fmt]])
 }
 
 _CACHE = {}
@@ -52,8 +70,8 @@ def compare(cfg, block_m=0, act=None, **kw):
     y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=block_m, act=act,
                      w2_input_scale=w2in, **kw)
     ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, act=act, l2_activation_scale=g2)
-    rel, excess = check_output(cfg.fmt, y, ref)
-    print(f"{cfg.name} bm={block_m}: max|err|/RMS = {rel:.3e}")
+    rel, excess, alt = check_layer(cfg.fmt, y, ref, x, ids, wts, w, num_shared=cfg.num_shared, act=act, g2=g2)
+    print(f"{cfg.name} bm={block_m}: max|err|/RMS = {rel:.3e}, tokens under another valid L2-input decision: {alt}")
     assert excess <= 0, (rel, excess)
     return y
 
@@ -67,6 +85,26 @@ def test_forward_matches_oracle(name):
 @pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small"])
 def test_forward_every_block_m(name, bm):
     compare(SMALL[name], block_m=bm)
+
+
+@pytest.mark.parametrize("bm", [32, 128])
+@pytest.mark.parametrize("name", sorted(MULTI))
+def test_forward_several_tiles_per_workgroup(name, bm):
+    compare(MULTI[name], block_m=bm)
+
+
+@pytest.mark.parametrize("name", sorted(MULTI))
+def test_forward_independent_of_block_m(name):
+    """Every output element's K sums run in the same order whatever the tile
+    height, so all BLOCK_M give bit-identical layers (a check of the tiling
+    and the copy pipeline that needs no tolerance)."""
+    cfg = MULTI[name]
+    x, ids, wts, w = inputs(cfg)
+    w2in, _ = l2_scale(cfg)
+    ys = [run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=bm, w2_input_scale=w2in)[0]
+          for bm in (32, 64, 128, 256)]
+    for bm, y in zip((64, 128, 256), ys[1:]):
+        assert np.array_equal(ys[0], y), bm
 
 
 def test_forward_activation_variants():
@@ -98,7 +136,7 @@ def test_forward_all_dropped_and_single_token():
     assert not y.any()
     y1, _ = run_layer("mxfp8", x[:1], ids[:1], wts[:1], w_r)
     ref1 = moe_reference("mxfp8", x[:1], ids[:1], wts[:1], w_r)
-    assert check_output("mxfp8", y1, ref1)[1] <= 0
+    assert check_layer("mxfp8", y1, ref1, x[:1], ids[:1], wts[:1], w_r)[1] <= 0
 
 
 @pytest.mark.parametrize("name", ["mxfp8_small", "nvfp4_small"])
