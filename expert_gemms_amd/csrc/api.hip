@@ -79,7 +79,7 @@ struct Workspace {
 };
 
 Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t n_sh, int64_t k, int64_t bm,
-               uint8_t* base) {
+               int64_t ksplit, uint8_t* base) {
   const int64_t E = n_loc + n_sh, S = T * (k + n_sh), M = S + E * (bm - 1);
   Workspace w;
   size_t off = 0;
@@ -106,7 +106,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   } else {
     w.a2 = take(M * I * 2);
   }
-  w.o = (float*)take(S * H * 4);
+  w.o = (float*)take(S * H * 4 * ksplit);
   w.bytes = off;
   return w;
 }
@@ -153,6 +153,43 @@ int block_m_rule(int T, int n_loc, int n_sh, int k, int fmt) {
   return best;
 }
 
+// The split rule counts rounds on a 256-CU part (MI355X); a host-only
+// constant, so workspace sizing and launches agree without a device query.
+constexpr int SPLIT_RULE_CUS = 256;
+
+// K splits of the L2 GEMM.  Its tiles (expected count at the rule's BLOCK_M)
+// run in rounds of one per CU; when the last round is partly empty, splitting
+// K into ks parts (each part's float32 result in its own buffer, added by the
+// combine) fills it at the price of (ks - 1) extra O writes and reads.  The
+// estimate takes the tile time from a nominal per-format MFMA rate; ks must
+// divide the stage count (and leave an even count per part where a stage is
+// half of a 128-K block-scale stage).  The choice does not depend on the
+// BLOCK_M a caller passes, so every BLOCK_M sums in the same order.
+int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int k, int cus) {
+  if (T <= 0 || cus <= 0) return 1;
+  const int bm = block_m_rule((int)T, n_loc, n_sh, k, fmt);
+  const double mtiles = n_loc * expected_padded((double)T * k / n_loc, bm) / bm +
+                        n_sh * (double)((T + bm - 1) / bm);
+  const double tiles = mtiles * (double)(H / GEMM_BN);
+  const int kst = fmt == MOE_FMT_BF16 ? 32 : (fmt == MOE_FMT_NVFP4 ? 128 : 64);
+  const int64_t nst = I / kst;
+  const double rate = (fmt == MOE_FMT_BF16 ? 1.0e15 : (fmt == MOE_FMT_NVFP4 ? 0.6e15 : 1.6e15)) / cus;
+  const double t_tile = 2.0 * bm * GEMM_BN * (double)I / rate;
+  const double S = (double)T * (k + n_sh);
+  int best = 1;
+  double best_t = 0.0;
+  for (int ks = 1; ks <= 4; ++ks) {
+    if (nst % ks) continue;
+    if (kst == 64 && ks > 1 && (nst / ks) % 2) continue;
+    const double t = std::ceil(tiles * ks / cus) * t_tile / ks + (ks - 1) * S * (double)H * 8.0 / 5.0e12;
+    if (ks == 1 || t < 0.97 * best_t) {   // a split must win by 3 %
+      best = ks;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   g_last_hip = e;
@@ -189,7 +226,8 @@ size_t moe_workspace_bytes(moe_format_t fmt, int max_tokens, int hidden, int int
     return 0;
   if (block_m == 0) block_m = 256;
   if (block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return 0;
-  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, nullptr).bytes;
+  const int ks = l2_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, ks, nullptr).bytes;
 }
 
 int moe_transform_weights(moe_format_t fmt, int num_experts, int hidden, int inter, const void* w13,
@@ -298,13 +336,15 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
   const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
   const int E = num_local_experts + num_shared;
-  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, nullptr).bytes > workspace_bytes)
+  int ks = l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, nullptr).bytes > workspace_bytes) ks = 1;
+  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, nullptr).bytes > workspace_bytes)
     return MOE_E_WORKSPACE;
   DeviceInfo* d;
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, (uint8_t*)workspace);
+  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, (uint8_t*)workspace);
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
@@ -362,6 +402,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.alpha = a.alpha;
   g.beta = a.beta;
   g.l2_scale = l2_activation_scale;
+  g.ksplit = 1;
   mark(2 * MOE_STEP_L1);
   hipError_t e = launch_gemm(fmt, 1, bm, g, grid, s);
   if (e != hipSuccess) return hip_status(e);
@@ -382,6 +423,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g2.N = (int)H;
   g2.K = (int)I;
   g2.o = w.o;
+  g2.ksplit = ks;
+  g2.o_split = (int64_t)T * kk * H;
   mark(2 * MOE_STEP_L2);
   e = launch_gemm(fmt, 2, bm, g2, grid, s);
   if (e != hipSuccess) return hip_status(e);
@@ -389,7 +432,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
 
   // a7: weighted combine
   mark(2 * MOE_STEP_COMBINE);
-  launch_combine(w.o, w.slot_row, topk_weights, num_tokens, top_k, (int)kk, (int)H, (uint16_t*)out, s);
+  launch_combine(w.o, ks, (int64_t)T * kk * H, w.slot_row, topk_weights, num_tokens, top_k, (int)kk, (int)H,
+                 (uint16_t*)out, s);
   mark(2 * MOE_STEP_COMBINE + 1);
   return hip_status(hipGetLastError());
 }

@@ -237,8 +237,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wm = w / G::WN, wn = w % G::WN;
   const int NB = p.N / GEMM_BN;
-  const int nstages = p.K / C::KSTAGE;
-  const int total = p.meta[0] * NB;
+  // L2 may split K: work unit u covers tile u % tiles and stages
+  // [ks * nstages, (ks + 1) * nstages) of K, ks = u / tiles
+  const int nstages = p.K / C::KSTAGE / p.ksplit;
+  const int tiles = p.meta[0] * NB;
+  const int total = tiles * p.ksplit;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
 
@@ -246,20 +249,35 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   // per-lane source offsets of its A rows.
   struct TileCtx {
     int e, nb, m0;
+    int s0;                 // first K stage of the work unit
+    int ks;                 // its K split
     int64_t a_off[G::A_INSTR];
     int64_t asf_off;
     const uint8_t* wexp;
     const uint8_t* wsf;
   };
-  auto make_tile = [&](int u) __attribute__((always_inline)) -> TileCtx {
+  auto make_tile = [&](int uu) __attribute__((always_inline)) -> TileCtx {
     TileCtx t;
-    // tile -> (expert, n block, m block)
-    int lo = 0, hi = p.num_experts - 1;
-    while (lo < hi) {  // largest e with tile_start(e) <= u
-      int mid = (lo + hi + 1) >> 1;
-      if ((p.offsets[mid] / BM) * NB <= u) lo = mid; else hi = mid - 1;
+    t.ks = uu / tiles;
+    t.s0 = t.ks * nstages;
+    const int u = uu - t.ks * tiles;
+    // tile -> (expert, n block, m block).  tile_start(e) = (offsets[e] / BM)
+    // * NB is non-decreasing, so the experts with tile_start <= u form a
+    // prefix and u's expert is its last member.  Lanes test 64 experts per
+    // load (four loads in flight), instead of a chain of dependent scalar
+    // loads.
+    int cnt = 0;
+    for (int b = 0; b < p.num_experts; b += 256) {
+      int ts[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = b + 64 * q + lane;
+        ts[q] = i < p.num_experts ? (p.offsets[i] / BM) * NB : 0x7FFFFFFF;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cnt += __builtin_popcountll(ballot(ts[q] <= u));
     }
-    const int e = lo;
+    const int e = cnt - 1;
     const int mb0 = p.offsets[e] / BM;
     const int mcount = p.offsets[e + 1] / BM - mb0;
     const int local = u - mb0 * NB;
@@ -305,35 +323,35 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
     constexpr int c = decltype(ci)::value;
     constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
     if constexpr (c < G::A_INSTR) {
-      g2lds16(p.a + t.a_off[c] + s * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
+      g2lds16(p.a + t.a_off[c] + (int64_t)(t.s0 + s) * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
     } else if constexpr (c < SC) {
       // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
       // global [layout stage][32-row block][KS_PER_L K-steps][FRAG]
       const int q = w * G::B_INSTR + (c - G::A_INSTR);
       const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
       const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
-      const int kg = s * C::STEPS + ksl;
+      const int kg = (t.s0 + s) * C::STEPS + ksl;
       const uint8_t* src = t.wexp + ((int64_t)(kg / C::KS_PER_L) * (p.N / 32) + t.nb * 8 + nf) * (C::KS_PER_L * C::FRAG) +
                            (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
       g2lds16(src, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
       // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
-      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + (s / G::SPL) * 4,
+      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + ((t.s0 + s) / G::SPL) * 4,
                                        (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
     } else if constexpr (!C::NV) {
       // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
-      const uint8_t* src = t.wsf + ((int64_t)(s / G::SPL) * (p.N / 32) + t.nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
+      const uint8_t* src = t.wsf + ((int64_t)((t.s0 + s) / G::SPL) * (p.N / 32) + t.nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
       g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
     } else if constexpr (c < SC + 2) {
       // NVFP4 A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM),
       // as two halves of 4 (64-K group 0, group 1)
       constexpr int h = c - SC;
-      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + s * 8 + 4 * h,
+      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + (t.s0 + s) * 8 + 4 * h,
                                        (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 * h + w * 256), 4, 0, 0);
     } else {
       // NVFP4 B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
       const int byte = (lane * 16) % (TN * 256);
-      const uint8_t* src = t.wsf + ((int64_t)s * (p.N / 32) + t.nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
+      const uint8_t* src = t.wsf + ((int64_t)(t.s0 + s) * (p.N / 32) + t.nb * 8 + wn * TN + byte / 256) * 256 + byte % 256;
       g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
     }
   };
@@ -613,7 +631,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
           const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
           const int slot = p.sorted_slot[row];
           if (slot < 0) continue;
-          float* orow = p.o + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
+          float* orow = p.o + ta.ks * p.o_split + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
         }

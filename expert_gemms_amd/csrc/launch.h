@@ -41,8 +41,11 @@ struct GemmArgs {
   int has_clamp;
   float clamp, alpha, beta;
   float l2_scale;          // NVFP4 global scale of the L2 input
-  // L2 epilogue: float32 rows per slot [S, H]
+  // L2 epilogue: float32 rows per slot [S, H]; with K split in ksplit parts
+  // (L2 only), part ks goes to o + ks * o_split
   float* o;
+  int ksplit;              // 1 for L1
+  int64_t o_split;
 };
 
 enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
@@ -54,8 +57,8 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
 hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t gemm_init(int device);
 
-void launch_combine(const float* o, const int32_t* slot_row, const float* topk_w, int T, int k, int kk,
-                    int H, uint16_t* out, hipStream_t stream);
+void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
+                    int T, int k, int kk, int H, uint16_t* out, hipStream_t stream);
 
 void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13_sf,
                       const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w13_k, uint8_t* w13_sf_k,
