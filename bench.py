@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--block-m", type=int, default=0, help="BLOCK_M (0: the library's rule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
+    p.add_argument("--route", action="store_true",
+                   help="time the router top-k (moe_route) on the workload's routing shape instead")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="only run a plain device copy of this many MB (HBM counter calibration)")
     return p.parse_args()
@@ -207,6 +209,72 @@ def default_cpu_tokens(cfg, T):
     return min(T, 4096) if cfg.E <= 16 else min(T, 4)
 
 
+# Router top-k settings per workload: (scoring, bias, groups, kept groups,
+# renormalise, scaling) -- DeepSeek-V3's sigmoid scores with correction bias
+# and 8 groups of which 4 are kept; softmax top-k elsewhere.
+ROUTE_STYLE = {
+    "tiny_bf16": ("softmax", False, 1, 1, True, 1.0),
+    "mixtral_bf16": ("softmax", False, 1, 1, True, 1.0),
+    "dsv3_mxfp8": ("sigmoid", True, 8, 4, True, 2.5),
+    "decode_mxfp4": ("softmax", False, 1, 1, True, 1.0),
+    "nvfp4_zipf": ("softmax", False, 1, 1, True, 1.0),
+}
+
+
+def route_bench(args, cfg, T):
+    """Router top-k on [T, E] float32 logits: tokens/s, HBM roofline, and the
+    oracle on the host for comparison."""
+    import expert_gemms_amd as moe
+    from oracle.routing import route_reference
+
+    scoring, use_bias, G, TG, renorm, scaling = ROUTE_STYLE[cfg.name]
+    E, k = cfg.E, cfg.top_k
+    rng = np.random.default_rng(cfg.cfg_id)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.05).astype(np.float32) if use_bias else None
+    dl = torch.from_numpy(logits).cuda()
+    db = None if bias is None else torch.from_numpy(bias).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    run = lambda: moe.moe_route(T, E, k, dl, ids, wts, bias=db, scoring=scoring, num_groups=G, topk_groups=TG,
+                                renormalize=renorm, routed_scaling_factor=scaling)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = T * E * 4 + T * k * 8 + (E * 4 if use_bias else 0)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = min(T, 8192)
+        t0, passes = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0:
+            route_reference(logits[:n].astype(np.float64), k, scoring=scoring,
+                            bias=None if bias is None else bias.astype(np.float64), num_groups=G,
+                            topk_groups=TG, renormalize=renorm, scaling=scaling)
+            passes += 1
+        dt = (time.perf_counter() - t0) / passes
+        cpu = {"value": round(n / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} of {T} tokens; {passes} pass(es), {dt:.3f} s per pass"}
+    rec = {"metric": "router top-k tokens/s", "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded N(0,1) router logits)",
+           "config": {"workload": cfg.name + " routing", "tokens": T, "experts": E, "top_k": k,
+                      "scoring": scoring, "bias": use_bias, "groups": G, "kept_groups": TG},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "router top-k"},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -222,6 +290,8 @@ def main():
     T = args.tokens if args.tokens is not None else cfg.T
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.route:
+        return route_bench(args, cfg, T)
     layer, x, ids, wts, ids_d, wts_d, canon = build_layer(cfg, T, device)
     out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=device)
     stream = torch.cuda.current_stream()

@@ -9,6 +9,6 @@ in torch-allocated device memory.
 from ._lib import (  # noqa: F401
     FMT, EXPORTS, Activation, MoEError, LIB_PATH, lib_handle,
     moe_get_block_m, moe_workspace_bytes, moe_transform_weights, moe_quantize_weights,
-    moe_quantize_x, moe_dispatch, moe_forward,
+    moe_quantize_x, moe_dispatch, moe_forward, moe_route,
 )
 from .layer import FusedMoE  # noqa: F401

@@ -19,7 +19,9 @@ OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 EXPORTS = (
     "moe_status_string", "moe_get_block_m", "moe_workspace_bytes", "moe_transform_weights",
     "moe_quantize_weights", "moe_quantize_x", "moe_dispatch", "moe_forward", "moe_forward_profiled",
+    "moe_route",
 )
+SCORING = {"softmax": 0, "sigmoid": 1}
 STEPS = ("quant_x", "dispatch", "l1", "l2", "combine")
 
 
@@ -65,6 +67,8 @@ def _lib():
         lib.moe_forward.restype = _I
         lib.moe_forward_profiled.argtypes = lib.moe_forward.argtypes + [_P]
         lib.moe_forward_profiled.restype = _I
+        lib.moe_route.argtypes = [_I, _I, _I, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P]
+        lib.moe_route.restype = _I
         _LIB = lib
     return _LIB
 
@@ -154,3 +158,14 @@ def moe_forward(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_e
         arr = (ctypes.c_void_p * len(step_events))(*[ctypes.c_void_p(e.cuda_event) for e in step_events])
         _check(_lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
     return out
+
+
+def moe_route(num_tokens, num_experts, top_k, logits, topk_ids, topk_weights, *, bias=None, scoring="softmax",
+              num_groups=1, topk_groups=1, renormalize=True, routed_scaling_factor=1.0, is_padding=None,
+              stream=None):
+    """Router top-k (``moe_route``): float32 logits [T, E] -> int32 ids and
+    float32 weights [T, top_k], written into the given tensors."""
+    _check(_lib().moe_route(num_tokens, num_experts, top_k, _ptr(logits), _ptr(bias), SCORING[scoring],
+                            num_groups, topk_groups, int(bool(renormalize)), float(routed_scaling_factor),
+                            _ptr(is_padding), _ptr(topk_ids), _ptr(topk_weights), _stream(stream)), "moe_route")
+    return topk_ids, topk_weights

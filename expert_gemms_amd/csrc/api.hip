@@ -305,6 +305,26 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start, in
   return hip_status(hipGetLastError());
 }
 
+int moe_route(int num_tokens, int num_experts, int top_k, const float* logits, const float* bias, int scoring,
+              int num_groups, int topk_groups, int renormalize, float routed_scaling_factor,
+              const uint8_t* is_padding, int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (num_tokens < 0 || num_experts < 1 || num_experts > 1024 || top_k < 1 || top_k > 64 || top_k > num_experts)
+    return MOE_E_INVALID;
+  if (scoring != MOE_SCORE_SOFTMAX && scoring != MOE_SCORE_SIGMOID) return MOE_E_INVALID;
+  if (num_groups < 1 || num_groups > 64 || num_experts % num_groups || topk_groups < 1 || topk_groups > num_groups)
+    return MOE_E_INVALID;
+  if (num_groups > 1 && (int64_t)topk_groups * (num_experts / num_groups) < top_k) return MOE_E_INVALID;
+  if (!isfinite(routed_scaling_factor)) return MOE_E_INVALID;
+  if (num_tokens == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_E_INVALID;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  launch_route(logits, bias, num_tokens, num_experts, top_k, scoring == MOE_SCORE_SIGMOID, num_groups, topk_groups,
+               renormalize != 0, routed_scaling_factor, is_padding, topk_ids, topk_weights, (hipStream_t)stream);
+  return hip_status(hipGetLastError());
+}
+
 int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
                          int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
                          const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,

@@ -75,6 +75,10 @@ void launch_quant_mx(bool fp4, bool f32, int64_t rows, int cols, const void* src
 void launch_quant_nv(bool f32, int64_t rows, int cols, const void* src, uint8_t* codes, uint8_t* scales,
                      float* row_g, const float* fixed_g, int rows_per_g, hipStream_t stream);
 
+void launch_route(const float* logits, const float* bias, int T, int E, int k, int sigmoid, int G, int TG,
+                  int renorm, float scaling, const uint8_t* is_padding, int32_t* ids, float* wts,
+                  hipStream_t stream);
+
 void launch_weight_gscale(int E, int64_t per_expert, const float* src, float* gscale, hipStream_t stream);
 
 }  // namespace moe

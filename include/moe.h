@@ -134,6 +134,35 @@ int moe_quantize_weights(moe_format_t fmt, int num_experts, int rows, int cols,
 int moe_quantize_x(moe_format_t fmt, int num_tokens, int hidden, const void* x,
                    void* codes, void* scales, float* token_scale, void* stream);
 
+/* Router top-k: float32 router logits [T, E] (device) -> topk_ids int32
+ * [T, top_k] and topk_weights float32 [T, top_k] (device), the input
+ * moe_forward takes.  The routing the "fused_moe" page's
+ * FusedMoE.select_experts dispatches to (fused_topk, fused_topk_bias,
+ * grouped_topk) and the padding-token skip of the DeepGEMM MegaMoE experts
+ * page's forward:
+ *   scores   softmax over the token's experts (MOE_SCORE_SOFTMAX) or the
+ *            sigmoid of each logit (MOE_SCORE_SIGMOID), float32
+ *   choice   score + bias[e] (bias: float32 [E] device, or NULL); the bias
+ *            only moves the choice
+ *   groups   num_groups contiguous groups of E / num_groups experts (1 = no
+ *            grouping); a group ranks by its best choice score and the
+ *            topk_groups best groups are kept
+ *   ids      the top_k kept experts by choice score, best first, ties to
+ *            the lower id (groups likewise)
+ *   weights  the chosen experts' unbiased scores, divided by their sum if
+ *            renormalize != 0, then times routed_scaling_factor
+ *   padding  is_padding: uint8 [T] (device) or NULL; a nonzero entry gives
+ *            the token ids -1 and weights 0, so moe_forward drops its slots
+ * 1 <= E <= 1024, 1 <= top_k <= min(E, 64), 1 <= topk_groups <= num_groups
+ * <= 64, num_groups divides E and the kept groups hold at least top_k
+ * experts; routed_scaling_factor finite.  MOE_E_INVALID otherwise (nothing
+ * enqueued); one wave per token. */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+int moe_route(int num_tokens, int num_experts, int top_k, const float* logits, const float* bias, int scoring,
+              int num_groups, int topk_groups, int renormalize, float routed_scaling_factor,
+              const uint8_t* is_padding, int32_t* topk_ids, float* topk_weights, void* stream);
+
 /* Routing metadata (the contiguous-layout permutation of the "fused_moe"
  * page's DeepGemmExperts.apply; groups padded to BLOCK_M as
  * compute_aligned_M does).  A slot is (token t, choice j), flat index

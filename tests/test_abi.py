@@ -129,3 +129,23 @@ def test_other_entry_points_validate():
     assert lib.moe_quantize_weights(1, 2, 64, 48, f, f, f, None, None) == _lib.E_INVALID
     assert lib.moe_transform_weights(0, 2, 200, 256, f, None, f, None, f, None, f, None, None) == _lib.E_INVALID
     assert lib.moe_transform_weights(1, 2, 256, 256, f, None, f, None, f, None, f, None, None) == _lib.E_INVALID
+
+
+def test_route_validates():
+    lib = moe.lib_handle()
+    P = ctypes.c_void_p
+    f = P(0x10000)
+    bad = [
+        (4, 0, 1, 0, 1, 1),       # no experts
+        (4, 8, 9, 0, 1, 1),       # top_k > E
+        (4, 2000, 8, 0, 1, 1),    # E > 1024
+        (4, 64, 8, 2, 1, 1),      # unknown scoring
+        (4, 64, 8, 1, 5, 1),      # groups do not divide E
+        (4, 64, 8, 1, 8, 9),      # topk_groups > num_groups
+        (4, 64, 8, 1, 16, 1),     # one kept group of 4 experts < top_k
+    ]
+    for T, E, k, sc, G, TG in bad:
+        assert lib.moe_route(T, E, k, f, None, sc, G, TG, 1, 1.0, None, f, f, None) == _lib.E_INVALID
+    assert lib.moe_route(4, 64, 8, f, None, 0, 1, 1, 1, float("inf"), None, f, f, None) == _lib.E_INVALID
+    assert lib.moe_route(4, 64, 8, None, None, 0, 1, 1, 1, 1.0, None, f, f, None) == _lib.E_INVALID
+    assert lib.moe_route(0, 64, 8, None, None, 0, 1, 1, 1, 1.0, None, None, None, None) == _lib.OK
