@@ -137,14 +137,45 @@ def quantize_l2_input(fmt, a, l2_activation_scale=1.0):
 # the layer
 # --------------------------------------------------------------------------
 
+def post_expert_norm(y, gamma, eps):
+    """The Muse-Spark MegaMoE page's post-expert RMSNorm, which its kernel
+    applies to the layer output (``post_expert_norm_gamma``,
+    ``post_expert_norm_eps``; the caller folds a zero-centred gain into
+    gamma): y / sqrt(mean over H of y^2 + eps) * gamma, float64."""
+    y = np.asarray(y, dtype=np.float64)
+    return y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def weight_on_input(x_bits, topk_weights):
+    """``apply_router_weight_on_input`` ("fused_moe" page, FusedMoE): each
+    token's (single) routing weight multiplies its BF16 input row, in float32
+    with one round to BF16, before the experts; the combine then weighs the
+    slot by 1."""
+    x32 = codecs.bf16_decode(x_bits).astype(np.float32)
+    w32 = np.asarray(topk_weights, dtype=np.float32)[:, :1]
+    return codecs.bf16_encode_f32((x32 * w32).astype(np.float32))
+
+
 def moe_reference(fmt, x_bits, topk_ids, topk_weights, w, *, num_shared=0,
                   expert_start=0, num_local=None, act=None,
-                  l2_activation_scale=1.0, tokens=None):
+                  l2_activation_scale=1.0, tokens=None, norm=None, router_weight_on_input=False):
     """float64 output [len(tokens), H] (all tokens if ``tokens`` is None).
 
     ``act`` is a dict with keys clamp (None or float), alpha, beta.
-    ``l2_activation_scale`` is the NVFP4 L2 global input scale.
+    ``l2_activation_scale`` is the NVFP4 L2 global input scale.  ``norm``:
+    None or (gamma [H], eps), the post-expert RMSNorm of the output.
+    ``router_weight_on_input``: top_k = 1 and no shared expert; the routing
+    weight scales the input instead of the expert output.
     """
+    if router_weight_on_input:
+        if np.asarray(topk_ids).shape[1] != 1 or num_shared:
+            raise ValueError("router weight on the input needs top_k = 1 and no shared expert")
+        x_bits = weight_on_input(x_bits, topk_weights)
+        topk_weights = np.ones_like(np.asarray(topk_weights, dtype=np.float64))
+        y = moe_reference(fmt, x_bits, topk_ids, topk_weights, w, num_shared=0, expert_start=expert_start,
+                          num_local=num_local, act=act, l2_activation_scale=l2_activation_scale,
+                          tokens=tokens)
+        return y if norm is None else post_expert_norm(y, *norm)
     if fmt not in FORMATS:
         raise ValueError(fmt)
     act = dict(act or {})
@@ -173,4 +204,4 @@ def moe_reference(fmt, x_bits, topk_ids, topk_weights, w, *, num_shared=0,
         W2 = dequant_weight(fmt, w, "w2", e)                   # [H, I]
         o = a_hat @ W2.T                                       # [n, H]
         np.add.at(y, r, wts[r, j][:, None] * o)
-    return y
+    return y if norm is None else post_expert_norm(y, *norm)
