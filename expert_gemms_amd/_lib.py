@@ -31,6 +31,13 @@ class MoEError(RuntimeError):
         super().__init__(f"{what}: {status} ({_lib().moe_status_string(status).decode()})")
 
 
+class Options(ctypes.Structure):
+    """``moe_options_t``: post-expert RMSNorm (gamma pointer, eps) and the
+    routing weight applied on the input."""
+    _fields_ = [("post_expert_norm_gamma", ctypes.c_void_p), ("post_expert_norm_eps", ctypes.c_float),
+                ("apply_router_weight_on_input", ctypes.c_int)]
+
+
 class Activation(ctypes.Structure):
     """``moe_activation_t``: swiglu with optional clamp, alpha, beta."""
     _fields_ = [("kind", ctypes.c_int), ("has_clamp", ctypes.c_int), ("clamp", ctypes.c_float),
@@ -62,7 +69,7 @@ def _lib():
         lib.moe_quantize_x.restype = _I
         lib.moe_dispatch.argtypes = [_I] * 6 + [_P] * 7
         lib.moe_dispatch.restype = _I
-        lib.moe_forward.argtypes = ([_I] * 9 + [ctypes.POINTER(Activation)] + [_P] * 9
+        lib.moe_forward.argtypes = ([_I] * 9 + [ctypes.POINTER(Activation), ctypes.POINTER(Options)] + [_P] * 9
                                     + [ctypes.c_float, _P, _P, ctypes.c_size_t, _P])
         lib.moe_forward.restype = _I
         lib.moe_forward_profiled.argtypes = lib.moe_forward.argtypes + [_P]
@@ -138,17 +145,23 @@ def moe_dispatch(num_tokens, top_k, num_shared, expert_start, num_local_experts,
 def moe_forward(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,
                 block_m, act, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k,
                 w13_gscale, w2_gscale, l2_activation_scale, out, workspace, workspace_bytes=None,
-                stream=None, step_events=None):
+                stream=None, step_events=None, norm_gamma=None, norm_eps=0.0, weight_on_input=False):
     """``step_events``: None, or 2 * len(STEPS) recorded torch.cuda.Event
-    objects (begin/end per step) -> calls moe_forward_profiled."""
+    objects (begin/end per step) -> calls moe_forward_profiled.
+    ``norm_gamma``/``norm_eps``: post-expert RMSNorm; ``weight_on_input``:
+    the routing weight scales the input (moe_options_t)."""
     a = None
     if act is not None:
         a = ctypes.byref(act if isinstance(act, Activation) else Activation(
             0, int(act.get("clamp") is not None), float(act.get("clamp") or 0.0),
             float(act.get("alpha", 1.0)), float(act.get("beta", 0.0))))
+    opts = None
+    if norm_gamma is not None or weight_on_input:
+        opts = ctypes.byref(Options(None if norm_gamma is None else norm_gamma.data_ptr(), float(norm_eps),
+                                    int(bool(weight_on_input))))
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     args = (_fmt(fmt), num_tokens, hidden, inter, top_k, expert_start, num_local_experts,
-            num_shared, block_m, a, _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+            num_shared, block_m, a, opts, _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
             _ptr(w13_k), _ptr(w13_sf_k), _ptr(w2_k), _ptr(w2_sf_k), _ptr(w13_gscale),
             _ptr(w2_gscale), float(l2_activation_scale), _ptr(out), _ptr(workspace),
             nbytes, _stream(stream))

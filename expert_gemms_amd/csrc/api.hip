@@ -75,6 +75,7 @@ struct Workspace {
   uint8_t* a2;        // L2 input codes
   uint8_t* a2_sf;     // L2 input block scales
   float* o;           // L2 output rows per slot
+  uint16_t* xw;       // BF16 input rows scaled by their routing weight
   size_t bytes;
 };
 
@@ -107,6 +108,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
     w.a2 = take(M * I * 2);
   }
   w.o = (float*)take(S * H * 4 * ksplit);
+  w.xw = (uint16_t*)take(T * H * 2);
   w.bytes = off;
   return w;
 }
@@ -327,7 +329,7 @@ int moe_route(int num_tokens, int num_experts, int top_k, const float* logits, c
 
 int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
                          int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
-                         const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
+                         const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
                          const void* w13_sf_k, const void* w2_k, const void* w2_sf_k, const float* w13_gscale,
                          const float* w2_gscale, float l2_activation_scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* ev) {
@@ -341,6 +343,13 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   moe_activation_t a = {MOE_ACT_SWIGLU, 0, 0.0f, 1.0f, 0.0f};
   if (act) a = *act;
   if (a.kind != MOE_ACT_SWIGLU) return MOE_E_UNSUPPORTED;
+  moe_options_t o = {nullptr, 0.0f, 0};
+  if (opts) o = *opts;
+  if (o.post_expert_norm_gamma &&
+      (!aligned16(o.post_expert_norm_gamma) || hidden > 16384 || !(o.post_expert_norm_eps >= 0.0f) ||
+       !isfinite(o.post_expert_norm_eps)))
+    return MOE_E_INVALID;
+  if (o.apply_router_weight_on_input && (top_k != 1 || num_shared != 0)) return MOE_E_INVALID;
   if (!isfinite(a.alpha) || !isfinite(a.beta) || (a.has_clamp && !(a.clamp >= 0.0f))) return MOE_E_INVALID;
   if (fmt == MOE_FMT_NVFP4 && (!(l2_activation_scale > 0.0f) || !isfinite(l2_activation_scale)))
     return MOE_E_INVALID;
@@ -369,12 +378,18 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
 
-  // a1: dispatch quantisation
+  // a1: dispatch quantisation (with the routing weight on the input, of the
+  // scaled rows)
   mark(2 * MOE_STEP_QUANT_X);
+  const void* xin = x;
+  if (o.apply_router_weight_on_input) {
+    launch_scale_rows((const uint16_t*)x, topk_weights, num_tokens, (int)H, w.xw, s);
+    xin = w.xw;
+  }
   if (fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4)
-    launch_quant_mx(false, false, T, (int)H, x, w.xq, w.xq_sf, s);
+    launch_quant_mx(false, false, T, (int)H, xin, w.xq, w.xq_sf, s);
   else if (fmt == MOE_FMT_NVFP4)
-    launch_quant_nv(false, T, (int)H, x, w.xq, w.xq_sf, w.x_tok, nullptr, 1, s);
+    launch_quant_nv(false, T, (int)H, xin, w.xq, w.xq_sf, w.x_tok, nullptr, 1, s);
   mark(2 * MOE_STEP_QUANT_X + 1);
   // a2: routing metadata
   mark(2 * MOE_STEP_DISPATCH);
@@ -390,7 +405,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
   const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (fmt == MOE_FMT_BF16) {
-    g.a = (const uint8_t*)x;
+    g.a = (const uint8_t*)xin;
     g.a_ld = H * 2;
   } else {
     g.a = w.xq;
@@ -452,19 +467,20 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
 
   // a7: weighted combine
   mark(2 * MOE_STEP_COMBINE);
-  launch_combine(w.o, ks, (int64_t)T * kk * H, w.slot_row, topk_weights, num_tokens, top_k, (int)kk, (int)H,
+  launch_combine(w.o, ks, (int64_t)T * kk * H, w.slot_row, o.apply_router_weight_on_input ? nullptr : topk_weights,
+                 num_tokens, top_k, (int)kk, (int)H, o.post_expert_norm_gamma, o.post_expert_norm_eps,
                  (uint16_t*)out, s);
   mark(2 * MOE_STEP_COMBINE + 1);
   return hip_status(hipGetLastError());
 }
 
 int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
-                int num_local_experts, int num_shared, int block_m, const moe_activation_t* act, const void* x,
-                const int32_t* topk_ids, const float* topk_weights, const void* w13_k, const void* w13_sf_k,
+                int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
+                const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k, const void* w13_sf_k,
                 const void* w2_k, const void* w2_sf_k, const float* w13_gscale, const float* w2_gscale,
                 float l2_activation_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_profiled(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,
-                              block_m, act, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale,
+                              block_m, act, opts, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale,
                               w2_gscale, l2_activation_scale, out, workspace, workspace_bytes, stream, nullptr);
 }
 

@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = 0; j < kk; ++j) {
     if (slot_row[s0 + j] < 0) continue;
-    const float wt = j < k ? topk_w[(int64_t)t * k + j] : 1.0f;
+    const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
     f32x4 v = *(const f32x4*)(o + (s0 + j) * H + h);
     for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + (s0 + j) * H + h);
     acc[0] += wt * v[0];
@@ -42,10 +42,78 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
   *(uint2*)(out + (int64_t)t * H + h) = packed;
 }
 
+// With the post-expert RMSNorm: one workgroup per token keeps the float32 row
+// in LDS, sums its squares, then writes y / sqrt(mean(y^2) + eps) * gamma.
+// The weighting matches k_combine element for element.
+__global__ void __launch_bounds__(256) k_combine_norm(const float* __restrict__ o, int nsplit, int64_t o_split,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ topk_w, int k, int kk, int H,
+                                                      const float* __restrict__ gamma, float eps,
+                                                      uint16_t* __restrict__ out) {
+  extern __shared__ f32x4 rowv[];   // H / 4
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int64_t s0 = (int64_t)t * kk;
+  float ss = 0.0f;
+  for (int h = threadIdx.x * 4; h < H; h += 1024) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < kk; ++j) {
+      if (slot_row[s0 + j] < 0) continue;
+      const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
+      f32x4 v = *(const f32x4*)(o + (s0 + j) * H + h);
+      for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + (s0 + j) * H + h);
+      acc[0] += wt * v[0];
+      acc[1] += wt * v[1];
+      acc[2] += wt * v[2];
+      acc[3] += wt * v[3];
+    }
+    rowv[h >> 2] = acc;
+    ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / __builtin_sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  for (int h = threadIdx.x * 4; h < H; h += 1024) {
+    const f32x4 acc = rowv[h >> 2];
+    const f32x4 g = *(const f32x4*)(gamma + h);
+    uint2 packed;
+    packed.x = (uint32_t)bf16_rne(acc[0] * r * g[0]) | ((uint32_t)bf16_rne(acc[1] * r * g[1]) << 16);
+    packed.y = (uint32_t)bf16_rne(acc[2] * r * g[2]) | ((uint32_t)bf16_rne(acc[3] * r * g[3]) << 16);
+    *(uint2*)(out + (int64_t)t * H + h) = packed;
+  }
+}
+
+// apply_router_weight_on_input: xw[t] = BF16(x[t] * w[t]) (top_k = 1), float32
+// product, one round to nearest even.
+__global__ void __launch_bounds__(256) k_scale_rows(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                    int H, uint16_t* __restrict__ xw) {
+  const int t = blockIdx.x;
+  const float s = w[t];
+  for (int h = threadIdx.x * 4; h < H; h += 1024) {
+    const uint2 v = *(const uint2*)(x + (int64_t)t * H + h);
+    const float a = u2f(v.x << 16) * s, b = u2f(v.x & 0xFFFF0000u) * s;
+    const float c = u2f(v.y << 16) * s, d = u2f(v.y & 0xFFFF0000u) * s;
+    uint2 r;
+    r.x = (uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16);
+    r.y = (uint32_t)bf16_rne(c) | ((uint32_t)bf16_rne(d) << 16);
+    *(uint2*)(xw + (int64_t)t * H + h) = r;
+  }
+}
+
 void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
-                    int T, int k, int kk, int H, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, stream, o, nsplit, o_split, slot_row,
-                     topk_w, k, kk, H, out);
+                    int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
+  if (gamma)
+    hipLaunchKernelGGL(k_combine_norm, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split, slot_row,
+                       topk_w, k, kk, H, gamma, eps, out);
+  else
+    hipLaunchKernelGGL(k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, stream, o, nsplit, o_split, slot_row,
+                       topk_w, k, kk, H, out);
+}
+
+void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream) {
+  hipLaunchKernelGGL(k_scale_rows, dim3(T), dim3(256), 0, stream, x, w, H, xw);
 }
 
 }  // namespace moe

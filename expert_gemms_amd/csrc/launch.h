@@ -57,8 +57,11 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
 hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t gemm_init(int device);
 
+// Combine (topk_w NULL: every slot weighs 1); gamma non-NULL adds the
+// post-expert RMSNorm.
 void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
-                    int T, int k, int kk, int H, uint16_t* out, hipStream_t stream);
+                    int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream);
+void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream);
 
 void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13_sf,
                       const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w13_k, uint8_t* w13_sf_k,

@@ -53,7 +53,11 @@ class FusedMoE:
             m = float(w2_input_scale.max()) if w2_input_scale is not None else 0.0
             self.l2_activation_scale = m if m > 0 else 1.0
 
-    def forward(self, x, topk_ids, topk_weights, out=None, block_m=0, stream=None, step_events=None):
+    def forward(self, x, topk_ids, topk_weights, out=None, block_m=0, stream=None, step_events=None,
+                norm_gamma=None, norm_eps=0.0, weight_on_input=False):
+        """``norm_gamma`` (float32 [H]) / ``norm_eps``: post-expert RMSNorm of
+        the output; ``weight_on_input``: the routing weight scales the input
+        (top_k = 1, no shared expert)."""
         T = x.shape[0]
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens, but the workspace was sized for {self.max_tokens}")
@@ -63,4 +67,5 @@ class FusedMoE:
                                 self.num_local_experts, self.num_shared, block_m, self.act, x, topk_ids,
                                 topk_weights, self.w13_k, self.w13_sf_k, self.w2_k, self.w2_sf_k,
                                 self.w13_gs, self.w2_gs, self.l2_activation_scale, out, self.workspace,
-                                stream=stream, step_events=step_events)
+                                stream=stream, step_events=step_events, norm_gamma=norm_gamma, norm_eps=norm_eps,
+                                weight_on_input=weight_on_input)

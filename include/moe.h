@@ -64,6 +64,23 @@ typedef struct {
   float beta;
 } moe_activation_t;
 
+/* Output-side options (NULL: none).
+ *   post_expert_norm_gamma  float32 [H] (device) or NULL: the output row is
+ *       RMS-normalised and scaled, y / sqrt(mean(y^2) + eps) * gamma, in
+ *       float32 before the BF16 rounding (the Muse-Spark MegaMoE page's
+ *       post_expert_norm_gamma / post_expert_norm_eps; a zero-centred gain
+ *       is folded into gamma by the caller).  hidden <= 16384; eps >= 0.
+ *   apply_router_weight_on_input  nonzero: each token's routing weight
+ *       multiplies its input row (float32, one BF16 rounding) before the
+ *       experts and the combine weighs the slot by 1 (the "fused_moe" page's
+ *       FusedMoE option of that name).  Needs top_k = 1 and no shared
+ *       expert. */
+typedef struct {
+  const float* post_expert_norm_gamma;
+  float post_expert_norm_eps;
+  int apply_router_weight_on_input;
+} moe_options_t;
+
 /* Human-readable text of a status code (a static string). */
 const char* moe_status_string(int status);
 
@@ -201,6 +218,7 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start,
  *                 every L2 input (the max over experts of w2 input_scale, or
  *                 1.0 if that max is 0), finite and > 0; ignored otherwise
  *   block_m       0 = moe_get_block_m(num_tokens, ...), else 32/64/128/256
+ *   act, opts     activation and output-side options, NULL for the defaults
  *   out           BF16 [T, H], fully overwritten            (device)
  *   workspace     >= moe_workspace_bytes(fmt, T, ..., block_m) bytes (device)
  * hidden, inter multiples of 128; 1 <= top_k; num_local_experts >= 1;
@@ -208,7 +226,7 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start,
  * may share a workspace, concurrent calls need their own. */
 int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
                 int expert_start, int num_local_experts, int num_shared, int block_m,
-                const moe_activation_t* act,
+                const moe_activation_t* act, const moe_options_t* opts,
                 const void* x, const int32_t* topk_ids, const float* topk_weights,
                 const void* w13_k, const void* w13_sf_k,
                 const void* w2_k, const void* w2_sf_k,
@@ -232,7 +250,7 @@ int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top
 #define MOE_NUM_STEPS 5
 int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
                          int expert_start, int num_local_experts, int num_shared, int block_m,
-                         const moe_activation_t* act,
+                         const moe_activation_t* act, const moe_options_t* opts,
                          const void* x, const int32_t* topk_ids, const float* topk_weights,
                          const void* w13_k, const void* w13_sf_k,
                          const void* w2_k, const void* w2_sf_k,

@@ -19,7 +19,7 @@ def x_dev(x_bits):
 
 
 def run_layer(fmt, x_bits, ids, wts, w, *, num_shared=0, expert_start=0, num_local=None, block_m=0,
-              act=None, w2_input_scale=None, max_tokens=None):
+              act=None, w2_input_scale=None, max_tokens=None, norm=None, weight_on_input=False):
     """Canonical NumPy inputs -> float64 NumPy output of moe_forward."""
     T, H = x_bits.shape
     E_all = w["w13"].shape[0]
@@ -33,6 +33,9 @@ def run_layer(fmt, x_bits, ids, wts, w, *, num_shared=0, expert_start=0, num_loc
                          dev(w["w13_gs"]) if "w13_gs" in w else None,
                          dev(w["w2_gs"]) if "w2_gs" in w else None,
                          w2_input_scale=None if w2_input_scale is None else torch.from_numpy(w2_input_scale))
-    out = layer.forward(x_dev(x_bits), dev(ids.astype(np.int32)), dev(wts.astype(np.float32)), block_m=block_m)
+    gamma = None if norm is None else torch.from_numpy(np.asarray(norm[0], dtype=np.float32)).cuda()
+    out = layer.forward(x_dev(x_bits), dev(ids.astype(np.int32)), dev(wts.astype(np.float32)), block_m=block_m,
+                        norm_gamma=gamma, norm_eps=0.0 if norm is None else float(norm[1]),
+                        weight_on_input=weight_on_input)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), layer

@@ -177,7 +177,7 @@ def decision_alternatives(fmt, a, da, g2=1.0):
 
 
 def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_start=0, num_local=None,
-                act=None, g2=1.0, tokens=None, max_decisions=12):
+                act=None, g2=1.0, tokens=None, max_decisions=12, norm=None, y_pre=None):
     """check_output, plus the boundary-decision rule above for tokens over
     the bar (every combination of a token's boundary decisions when there are
     at most ``max_decisions``, else a greedy search).  ``tokens``: the token
@@ -192,6 +192,13 @@ def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_
 
     def row_excess(yg, yr):
         return float((np.abs(yg - yr) - (TOL[fmt] * rms + bf16_half_ulp(yr))).max())
+
+    def post(r, delta):
+        """the oracle row r with the pre-norm change delta"""
+        if norm is None:
+            return y_ref[r] + delta
+        from oracle.moe import post_expert_norm
+        return post_expert_norm(y_pre[r] + delta, *norm)
 
     tok = np.arange(y_ref.shape[0]) if tokens is None else np.asarray(tokens)
     E_all = w["w13"].shape[0]
@@ -225,21 +232,22 @@ def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_
             # every combination
             for n in range(1, len(deltas) + 1):
                 for combo in itertools.combinations(deltas, n):
-                    best = min(best, row_excess(y_gpu[r], y_ref[r] + np.sum(combo, axis=0)))
+                    best = min(best, row_excess(y_gpu[r], post(r, np.sum(combo, axis=0))))
         elif deltas:
             # too many to enumerate: add, one at a time, the decision that
             # brings the oracle closest (2-norm) to the GPU row, while it helps
-            cur = y_ref[r].copy()
+            acc = np.zeros_like(y_ref[r])
             left = list(range(len(deltas)))
             for _ in range(max_decisions):
+                cur = post(r, acc)
                 if row_excess(y_gpu[r], cur) <= 0 or not left:
                     break
-                norms = [np.linalg.norm(y_gpu[r] - cur - deltas[i]) for i in left]
+                norms = [np.linalg.norm(y_gpu[r] - post(r, acc + deltas[i])) for i in left]
                 i = int(np.argmin(norms))
                 if norms[i] >= np.linalg.norm(y_gpu[r] - cur):
                     break
-                cur += deltas[left.pop(i)]
-            best = min(best, row_excess(y_gpu[r], cur))
+                acc = acc + deltas[left.pop(i)]
+            best = min(best, row_excess(y_gpu[r], post(r, acc)))
         if best <= 0:
             rescued += 1
         worst = max(worst, best)

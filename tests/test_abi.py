@@ -81,14 +81,15 @@ class _Fake:
 
 def _fwd(**kw):
     lib = moe.lib_handle()
-    a = dict(fmt=0, T=4, H=256, I=256, k=2, start=0, nloc=4, nsh=0, bm=0, act=None,
+    a = dict(fmt=0, T=4, H=256, I=256, k=2, start=0, nloc=4, nsh=0, bm=0, act=None, opts=None,
              x=_Fake(), ids=_Fake(), wts=_Fake(), w13=_Fake(), w13sf=None, w2=_Fake(), w2sf=None,
              g13=None, g2=None, l2=1.0, out=_Fake(), ws=_Fake(), wsb=1 << 40)
     a.update(kw)
     p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
     act = ctypes.byref(a["act"]) if a["act"] is not None else None
+    opts = ctypes.byref(a["opts"]) if a["opts"] is not None else None
     return lib.moe_forward(a["fmt"], a["T"], a["H"], a["I"], a["k"], a["start"], a["nloc"], a["nsh"], a["bm"],
-                           act, p(a["x"]), p(a["ids"]), p(a["wts"]), p(a["w13"]), p(a["w13sf"]), p(a["w2"]),
+                           act, opts, p(a["x"]), p(a["ids"]), p(a["wts"]), p(a["w13"]), p(a["w13sf"]), p(a["w2"]),
                            p(a["w2sf"]), p(a["g13"]), p(a["g2"]), a["l2"], p(a["out"]), p(a["ws"]),
                            a["wsb"], None)
 
@@ -102,6 +103,11 @@ def _fwd(**kw):
     dict(act=_lib.Activation(0, 0, 0.0, float("inf"), 0.0)),
     dict(act=_lib.Activation(0, 1, -1.0, 1.0, 0.0)),
     dict(nloc=999, nsh=2),                       # more than 1000 local experts
+    dict(opts=_lib.Options(0x10000, -1.0, 0)),   # negative norm eps
+    dict(opts=_lib.Options(0x10004, 1e-6, 0)),   # unaligned gamma
+    dict(opts=_lib.Options(0x10000, 1e-6, 0), H=16640),   # norm row does not fit LDS
+    dict(opts=_lib.Options(None, 0.0, 1)),       # weight on input with top_k = 2
+    dict(opts=_lib.Options(None, 0.0, 1), k=1, nsh=1),     # ... or with a shared expert
 ])
 def test_forward_rejects_invalid_arguments(kw):
     assert _fwd(**kw) == _lib.E_INVALID

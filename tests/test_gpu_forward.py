@@ -147,3 +147,35 @@ def test_forward_deterministic(name):
     a, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
     b, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small"])
+def test_forward_post_expert_norm(name):
+    """Post-expert RMSNorm fused into the combine (Muse-Spark MegaMoE page)."""
+    cfg = SMALL[name]
+    x, ids, wts, w = inputs(cfg)
+    w2in, g2 = l2_scale(cfg)
+    gamma = np.random.default_rng(7).uniform(0.5, 1.5, cfg.H)
+    norm = (gamma, 1e-6)
+    y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in, norm=norm)
+    pre = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, l2_activation_scale=g2)
+    ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, l2_activation_scale=g2, norm=norm)
+    rel, excess, alt = check_layer(cfg.fmt, y, ref, x, ids, wts, w, num_shared=cfg.num_shared, g2=g2, norm=norm,
+                                   y_pre=pre)
+    print(f"{name} + norm: max|err|/RMS = {rel:.3e}, tokens under another valid decision: {alt}")
+    assert excess <= 0, (rel, excess)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8", "mxfp4", "nvfp4"])
+def test_forward_router_weight_on_input(fmt):
+    """apply_router_weight_on_input (top_k = 1, no shared expert)."""
+    from oracle.moe import weight_on_input
+    cfg = MoEConfig(f"woi_{fmt}", 50, fmt, 300, 512, 256, 8, 1, routing="softmax_uniform")
+    x, ids, wts, w = inputs(cfg)
+    wts = np.random.default_rng(8).uniform(0.2, 1.0, ids.shape).astype(np.float32)
+    w2in, g2 = l2_scale(cfg)
+    y, _ = run_layer(fmt, x, ids, wts, w, w2_input_scale=w2in, weight_on_input=True)
+    ref = moe_reference(fmt, x, ids, wts, w, l2_activation_scale=g2, router_weight_on_input=True)
+    rel, excess, alt = check_layer(fmt, y, ref, weight_on_input(x, wts), ids, np.ones_like(wts), w, g2=g2)
+    print(f"{fmt} weight on input: max|err|/RMS = {rel:.3e}, tokens under another valid decision: {alt}")
+    assert excess <= 0, (rel, excess)
