@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--flush-mb", type=int, default=0, help="write this many MB between steps (defeats the MALL)")
     p.add_argument("--block-m", type=int, default=0, help="BLOCK_M (0: the library's rule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     p.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     p.add_argument("--route", action="store_true",
                    help="time the router top-k (moe_route) on the workload's routing shape instead")
@@ -309,24 +310,61 @@ def main():
         layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
     torch.cuda.synchronize()
 
+    # timed: K plain steps (with --flush-mb, each step is timed on its own so
+    # the flush stays outside)
+    fwd = lambda: layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
+    wall0 = time.perf_counter()
+    if flush is None:
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for i in range(args.steps):
+            fwd()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            evs[i][0].record(stream)
+            fwd()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    wall = time.perf_counter() - wall0
+
+    # per-step device times (the library records HIP events around each step
+    # on its launch stream), from K more steps
     step_events = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record(stream)
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
         layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m, step_events=step_events[i])
-    t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
     per_step = {name: float(np.mean([ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in step_events]))
                 for j, name in enumerate(moe._lib.STEPS)}
-    step_ms = [ev[0].elapsed_time(ev[2 * nsteps - 1]) for ev in step_events]
-    ms_per_step = float(np.mean(step_ms)) if flush is not None else t_start.elapsed_time(t_end) / args.steps
+
+    # secondary: the step captured once in a HIP graph and replayed (launch
+    # overhead removed); the replay's output is checked against the eager one
+    graph_ms = None
+    if not args.no_graph:
+        ref_out = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fwd()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("graph replay differs from the eager step")
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
 
     flops, hbm_bytes, l1_flops, l1_wbytes, touched = algorithmic(cfg, T, ids)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -377,6 +415,7 @@ def main():
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "mfma_frac": round(tflops / peak, 4),
         "step_ms": {k: round(v, 4) for k, v in per_step.items()},
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "wall_s": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -179,3 +179,39 @@ def test_forward_router_weight_on_input(fmt):
     rel, excess, alt = check_layer(fmt, y, ref, weight_on_input(x, wts), ids, np.ones_like(wts), w, g2=g2)
     print(f"{fmt} weight on input: max|err|/RMS = {rel:.3e}, tokens under another valid decision: {alt}")
     assert excess <= 0, (rel, excess)
+
+
+@pytest.mark.parametrize("name", ["nvfp4_small", "mxfp8_multi_i1024"])
+def test_forward_graph_replay(name):
+    """One forward captured in a HIP graph and replayed three times, with
+    eager forwards of other inputs on the same workspace in between: every
+    replay equals the eager result bit for bit (no step reads workspace left
+    by an earlier call)."""
+    from tests.gpu_util import dev, x_dev
+    cfg = {**SMALL, **MULTI}[name]
+    x, ids, wts, w = inputs(cfg)
+    w2in, _ = l2_scale(cfg)
+    _, layer = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
+    xd, idd, wd = x_dev(x), dev(ids.astype(np.int32)), dev(wts.astype(np.float32))
+    eager = layer.forward(xd, idd, wd).clone()
+    # other inputs: the tokens reversed and fewer of them
+    T2 = max(1, cfg.T // 2)
+    x2, id2, w2 = x_dev(x[::-1][:T2]), dev(ids[::-1][:T2].astype(np.int32)), dev(wts[::-1][:T2].astype(np.float32))
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(xd, idd, wd, out=out)          # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(xd, idd, wd, out=out)
+    for i in range(3):
+        out.zero_()
+        other = layer.forward(x2, id2, w2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        assert other.abs().sum() > 0
