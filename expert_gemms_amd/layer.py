@@ -34,6 +34,7 @@ class FusedMoE:
         self.w13_k = self.w2_k = self.w13_sf_k = self.w2_sf_k = None
         self.w13_gs = self.w2_gs = None
         self.l2_activation_scale = 1.0
+        self.norm_gamma, self.norm_eps = None, 0.0
 
     def load_canonical(self, w13, w2, w13_sf=None, w2_sf=None, w13_gs=None, w2_gs=None,
                        w2_input_scale=None, stream=None):
@@ -53,11 +54,26 @@ class FusedMoE:
             m = float(w2_input_scale.max()) if w2_input_scale is not None else 0.0
             self.l2_activation_scale = m if m > 0 else 1.0
 
+    def set_post_expert_norm(self, weight, eps, gain_center=None):
+        """Post-expert RMSNorm applied by every later ``forward``.  The library
+        applies gamma as given, so a zero-centred gain (the stored weight is
+        the offset from ``gain_center``) is folded in here, once, as the
+        Muse-Spark MegaMoE page's holder does before its kernel runs."""
+        gamma = weight.to(self.device, torch.float32)
+        if gain_center is not None:
+            gamma = gamma + float(gain_center)
+        self.norm_gamma, self.norm_eps = gamma.contiguous(), float(eps)
+
     def forward(self, x, topk_ids, topk_weights, out=None, block_m=0, stream=None, step_events=None,
-                norm_gamma=None, norm_eps=0.0, weight_on_input=False):
+                norm_gamma=None, norm_eps=None, weight_on_input=False):
         """``norm_gamma`` (float32 [H]) / ``norm_eps``: post-expert RMSNorm of
-        the output; ``weight_on_input``: the routing weight scales the input
+        the output (default: what ``set_post_expert_norm`` stored, if
+        anything); ``weight_on_input``: the routing weight scales the input
         (top_k = 1, no shared expert)."""
+        if norm_gamma is None:
+            norm_gamma = self.norm_gamma
+            norm_eps = self.norm_eps if norm_eps is None else norm_eps
+        norm_eps = 0.0 if norm_eps is None else norm_eps
         T = x.shape[0]
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens, but the workspace was sized for {self.max_tokens}")

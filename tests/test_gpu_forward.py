@@ -215,3 +215,23 @@ def test_forward_graph_replay(name):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         assert other.abs().sum() > 0
+
+
+def test_forward_norm_zero_centred_gain_folded_by_holder():
+    """set_post_expert_norm(weight, eps, gain_center) ≡ passing gamma =
+    weight + gain_center to forward, bit for bit."""
+    from tests.gpu_util import dev, x_dev
+    cfg = SMALL["bf16_small"]
+    x, ids, wts, w = inputs(cfg)
+    _, layer = run_layer(cfg.fmt, x, ids, wts, w)
+    gamma = torch.from_numpy(np.random.default_rng(7).uniform(0.5, 1.5, cfg.H).astype(np.float32))
+    xd, idd, wd = x_dev(x), dev(ids.astype(np.int32)), dev(wts.astype(np.float32))
+    direct = layer.forward(xd, idd, wd, norm_gamma=gamma.cuda(), norm_eps=1e-6)
+    layer.set_post_expert_norm(gamma - 1.0, 1e-6, gain_center=1.0)
+    folded = layer.forward(xd, idd, wd)
+    torch.cuda.synchronize()
+    # gamma - 1 + 1 may differ from gamma in its last bit; compare against that gamma
+    g2 = (gamma - 1.0) + 1.0
+    again = layer.forward(xd, idd, wd, norm_gamma=g2.cuda(), norm_eps=1e-6)
+    assert torch.equal(folded, again)
+    assert torch.allclose(folded.float(), direct.float(), rtol=1e-2, atol=1e-2)
