@@ -173,7 +173,7 @@ int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
   const double mtiles = n_loc * expected_padded((double)T * k / n_loc, bm) / bm +
                         n_sh * (double)((T + bm - 1) / bm);
   const double tiles = mtiles * (double)(H / GEMM_BN);
-  const int kst = fmt == MOE_FMT_BF16 ? 32 : (fmt == MOE_FMT_NVFP4 ? 128 : 64);
+  const int kst = fmt == MOE_FMT_BF16 ? 32 : 128;
   const int64_t nst = I / kst;
   const double rate = (fmt == MOE_FMT_BF16 ? 1.0e15 : (fmt == MOE_FMT_NVFP4 ? 0.6e15 : 1.6e15)) / cus;
   const double t_tile = 2.0 * bm * GEMM_BN * (double)I / rate;
@@ -182,7 +182,6 @@ int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
   double best_t = 0.0;
   for (int ks = 1; ks <= 4; ++ks) {
     if (nst % ks) continue;
-    if (kst == 64 && ks > 1 && (nst / ks) % 2) continue;
     const double t = std::ceil(tiles * ks / cus) * t_tile / ks + (ks - 1) * S * (double)H * 8.0 / 5.0e12;
     if (ks == 1 || t < 0.97 * best_t) {   // a split must win by 3 %
       best = ks;

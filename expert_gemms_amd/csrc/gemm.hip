@@ -51,15 +51,17 @@ template <> struct FmtCfg<F_BF16> {
   static constexpr int FRAG = 1024, KS_PER_L = 4;
   static constexpr bool SCALED = false, NV = false;
 };
-// MX formats: one 64-K scaled-MFMA step per stage; block scales keep their
-// 128-K layout stages (SC_HALF: a stage uses half of its layout stage's scales).
+// MX formats: a stage is one 128-K block-scale layout stage, two 64-K
+// scaled-MFMA steps (K-step j takes A-scale byte 2j + lane group and B-scale
+// byte j of the layout stage); fewer, longer stages amortise each stage's
+// wait, barrier and scale reads.
 template <> struct FmtCfg<F_MXFP8> {
-  static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 64, STEPS = 1, NBUF = 4;
+  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 128, STEPS = 2, NBUF = 3;
   static constexpr int FRAG = 2048, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = false;
 };
 template <> struct FmtCfg<F_MXFP4> {
-  static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 32, STEPS = 1, NBUF = 4;
+  static constexpr int KSTAGE = 128, A_ROW = 128, B_ROW = 64, STEPS = 2, NBUF = 4;
   static constexpr int FRAG = 1024, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = false;
 };
@@ -67,6 +69,15 @@ template <> struct FmtCfg<F_NVFP4> {
   static constexpr int KSTAGE = 128, A_ROW = 64, B_ROW = 64, STEPS = 2, NBUF = 4;
   static constexpr int FRAG = 1024, KS_PER_L = 2;
   static constexpr bool SCALED = true, NV = true;
+};
+
+// Configuration per tile height: the format's, except MXFP8 with 256-row
+// tiles, whose 128-K stages would not fit three times in LDS.  Those take
+// 64-K stages of one scaled K-step, whose scales are one half of the 128-K
+// layout stage's, chosen by the stage's parity.
+template <int FMT, int BM> struct Cfg : FmtCfg<FMT> {};
+template <> struct Cfg<F_MXFP8, 256> : FmtCfg<F_MXFP8> {
+  static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 64, STEPS = 1, NBUF = 4;
 };
 
 __device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
@@ -80,7 +91,7 @@ __device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p)
 
 template <int FMT, int BM>
 struct TileGeom {
-  using C = FmtCfg<FMT>;
+  using C = Cfg<FMT, BM>;
   static constexpr int WM = BM >= 128 ? 2 : 1;
   static constexpr int WN = 4 / WM;
   static constexpr int TM = BM / WM / 32;
@@ -94,11 +105,12 @@ struct TileGeom {
   static constexpr int A_SF_STAGE = C::SCALED ? (C::NV ? 2 : 1) * 4 * 256 : 0;
   static constexpr int B_SF_STAGE = C::SCALED ? 4 * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
-  // LDS stage buffers: the format's ring depth for the large (MFMA-bound)
-  // tiles; as many as fit, up to 8, for the small tiles of weight-streaming
-  // launches, whose stages are short and need more copies in flight.
+  // LDS stage buffers: the format's ring depth (or as many as fit) for the
+  // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
+  // weight-streaming launches, whose stages are short and need more copies in
+  // flight.
   static constexpr int NBUF_FIT = (160 * 1024 - (C::NV ? 1024 : 0)) / STAGE;
-  static constexpr int NBUF = BM >= 128 ? C::NBUF : (NBUF_FIT < 8 ? NBUF_FIT : 8);
+  static constexpr int NBUF = BM >= 128 ? (C::NBUF < NBUF_FIT ? C::NBUF : NBUF_FIT) : (NBUF_FIT < 8 ? NBUF_FIT : 8);
   static constexpr int ROWS_OFF = NBUF * STAGE;      // per-row epilogue scales (NVFP4)
   static constexpr int LDS = NBUF * STAGE + (C::NV ? 1024 : 0);
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
@@ -114,12 +126,13 @@ struct TileGeom {
   static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
   // kernel stages per 128-K stage of the block-scale layouts
   static constexpr int SPL = 128 / C::KSTAGE;
-  static_assert(!C::SCALED || C::NV || (SPL == 2 && C::STEPS == 1), "MX scale halves follow the stage parity");
+  static_assert(!C::SCALED || C::NV || (SPL == 2 && C::STEPS == 1) || (SPL == 1 && C::STEPS == 2),
+                "MX stages are one 128-K layout stage or one half of it");
   static_assert(TN % 2 == 0, "gate/up pairs need an even number of N fragments");
 };
 
-// LDS A rows are 128 bytes (8 chunks of 16 bytes) or, for NVFP4, 64 bytes
-// (4 chunks).  gfx950 LDS serves 16 lanes x 16 bytes per cycle from 64 banks,
+// LDS A rows are 128 bytes (8 chunks of 16 bytes: MX 128-K stages) or 64
+// bytes (4 chunks: BF16, NVFP4, MXFP8 256-row tiles).  gfx950 LDS serves 16 lanes x 16 bytes per cycle from 64 banks,
 // so the 16 rows a ds_read_b128 phase touches must land on 16 distinct
 // 16-byte bank groups: the chunk index is XORed with (r >> 1) & 7 for
 // 128-byte rows (rows r, r+1 already differ by 128 bytes) and with
@@ -137,7 +150,7 @@ template <> struct Frag<F_MXFP8> { using A = i32x8; using B = i32x8; };
 template <> struct Frag<F_MXFP4> { using A = i32x8; using B = i32x8; };
 template <> struct Frag<F_NVFP4> { using A = i32x4; using B = i32x4; };   // raw E2M1, 32 values
 
-template <int FMT, int TM, int TN, typename C = FmtCfg<FMT>>
+template <int FMT, int TM, int TN, typename C>
 __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int ks, int wm, int wn, int lane,
                                            typename Frag<FMT>::A (&af)[TM], typename Frag<FMT>::B (&bf)[TN]) {
   const int g = lane >> 5, l32 = lane & 31;
@@ -225,13 +238,17 @@ __device__ __forceinline__ void boundary_hint() {
 
 template <int FMT, int BM, int LAYER>
 __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_gemm(const GemmArgs p) {
-  using C = FmtCfg<FMT>;
   using G = TileGeom<FMT, BM>;
+  using C = typename G::C;
   using FA = typename Frag<FMT>::A;
   using FB = typename Frag<FMT>::B;
   constexpr int TM = G::TM, TN = G::TN;
   constexpr int READS = FMT == F_NVFP4 ? TM + TN : TM * (FMT == F_BF16 ? 1 : 2) + TN * (FMT == F_MXFP8 ? 2 : 1);
-  constexpr int SA_N = C::NV ? 2 * TM : TM;   // A-scale dwords held per stage
+  // scale registers held per stage: NVFP4 two dwords of 4 E4M3 A scales per
+  // row block and one dword of B scales per column block; MX one UE8M0 byte
+  // per row / column block and K-step
+  constexpr int SA_N = C::NV ? 2 * TM : C::STEPS * TM;
+  constexpr int SB_N = C::NV ? TN : C::STEPS * TN;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -362,12 +379,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   };
 
   f32x16 acc[TM][TN];   // the tile's accumulators (AGPRs)
-  // Block scales of a stage (in buffer st) of parity PAR.  MX: the one
-  // UE8M0 byte each lane hands its scaled MFMA (a 64-K stage uses half of
-  // its 128-K layout stage's scales; lane group g takes A block 2*PAR + g),
-  // read as bytes so no VALU work waits on the LDS read.  NVFP4: dwords of
-  // 4 E4M3 scales.
-  auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[TN])
+  // Block scales of a stage (in buffer st) of parity PAR.  MX: for each
+  // K-step, the one UE8M0 byte each lane hands its scaled MFMA: K-step kl of
+  // the 128-K layout stage (kl = the K-step, or for 64-K stages the stage
+  // parity) takes A block 2*kl + g and B byte kl; read as bytes so no VALU
+  // work waits on the LDS read.  NVFP4: dwords of 4 E4M3 scales.
+  auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[SB_N])
       __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;
     if constexpr (C::SCALED) {
@@ -380,18 +397,29 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
           sa[tm] = *(const uint32_t*)(Asf + r * 4);
           sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
         } else {
-          sa[tm] = Asf[r * 4 + 2 * PAR + g];
+#pragma unroll
+          for (int ks = 0; ks < C::STEPS; ++ks) {
+            const int kl = C::STEPS == 1 ? PAR : ks;
+            sa[ks * TM + tm] = Asf[r * 4 + 2 * kl + g];
+          }
         }
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        if constexpr (C::NV) sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
-        else sb[tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + PAR];
+        if constexpr (C::NV) {
+          sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < C::STEPS; ++ks) {
+            const int kl = C::STEPS == 1 ? PAR : ks;
+            sb[ks * TN + tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + kl];
+          }
+        }
       }
     }
   };
   auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
-                   const uint32_t (&sb)[TN]) __attribute__((always_inline)) {
+                   const uint32_t (&sb)[SB_N]) __attribute__((always_inline)) {
     if constexpr (C::NV) {
       // 64-K group ks: four 16-wide K-steps; sub-step j takes the lane's
       // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
@@ -427,9 +455,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
           if constexpr (FMT == F_BF16) {
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
           } else {
-            static_assert(C::STEPS == 1, "MX stages hold one scaled K-step");
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[tm], 0, (int)sb[tn]);
+                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[ks * TM + tm], 0,
+                (int)sb[ks * TN + tn]);
           }
         }
       }
@@ -488,11 +516,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
 
     FA af[2][TM];
     FB bfr[2][TN];
-    uint32_t sa4[SA_N] = {}, sb2[TN] = {}, sa4n[SA_N] = {}, sb2n[TN] = {};
+    uint32_t sa4[SA_N] = {}, sb2[SB_N] = {}, sa4n[SA_N] = {}, sb2n[SB_N] = {};
     {
       const uint8_t* st0 = smem + cur * G::STAGE;
       read_scales(st0, IC<0>{}, sa4, sb2);
-      load_frags<FMT, TM, TN>(st0, st0 + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
+      load_frags<FMT, TM, TN, C>(st0, st0 + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
     }
     constexpr int MF = TM * TN * (C::NV ? 4 : 1);   // MFMAs per K-step
     // One stage.  RB: register set holding the stage's first K-step
@@ -517,7 +545,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         constexpr int ks = decltype(kc)::value;
         constexpr int lo = ks * G::CPS / C::STEPS, hi = (ks + 1) * G::CPS / C::STEPS;
         constexpr int r0 = (RB + ks) & 1, r1 = (RB + ks + 1) & 1;
-        load_frags<FMT, TM, TN>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
+        load_frags<FMT, TM, TN, C>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
         issue(IC<lo>{}, IC<hi>{}, tf, js, fill);
         mfmas(ks, af[r0], bfr[r0], sa4, sb2);
         boundary_hint<READS, MF, hi - lo>();
@@ -534,16 +562,16 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
         const uint8_t* nx = smem + nxt * G::STAGE;
         // with one K-step per stage, RB is the stage's parity
         read_scales(nx, IC<(RB + 1) & 1>{}, sa4n, sb2n);
-        load_frags<FMT, TM, TN>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
+        load_frags<FMT, TM, TN, C>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
       }
       issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
       mfmas(C::STEPS - 1, af[rl], bfr[rl], sa4, sb2);
-      boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + TN : 0), MF, G::CPS - LAST>();
+      boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + SB_N : 0), MF, G::CPS - LAST>();
       if constexpr (!LASTS) {
 #pragma unroll
         for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) sb2[tn] = sb2n[tn];
+        for (int tn = 0; tn < SB_N; ++tn) sb2[tn] = sb2n[tn];
       }
       cur = nxt;
     };
