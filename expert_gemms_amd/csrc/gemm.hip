@@ -109,7 +109,12 @@ struct TileGeom {
   // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
   // weight-streaming launches, whose stages are short and need more copies in
   // flight.
-  static constexpr int NBUF_FIT = (160 * 1024 - (C::NV ? 1024 : 0)) / STAGE;
+  // workgroups per CU: two for the small tiles of weight-streaming launches
+  // when three stage buffers each fit in half the LDS (while one workgroup
+  // waits at a stage boundary the other computes or issues copies), else
+  // one (the MFMA-bound tiles also need every register)
+  static constexpr int OCC = BM <= 64 && 3 * STAGE + (C::NV ? 1024 : 0) <= 80 * 1024 ? 2 : 1;
+  static constexpr int NBUF_FIT = (160 * 1024 / OCC - (C::NV ? 1024 : 0)) / STAGE;
   static constexpr int NBUF = BM >= 128 ? (C::NBUF < NBUF_FIT ? C::NBUF : NBUF_FIT) : (NBUF_FIT < 8 ? NBUF_FIT : 8);
   static constexpr int ROWS_OFF = NBUF * STAGE;      // per-row epilogue scales (NVFP4)
   static constexpr int LDS = NBUF * STAGE + (C::NV ? 1024 : 0);
@@ -123,7 +128,7 @@ struct TileGeom {
   static_assert((NBUF - 2) * CPS < 64, "vmcnt holds 6 bits");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1, "tile too small");
   static_assert(NBUF >= 3, "the copies of stage s + NBUF - 1 are spread over stage s");
-  static_assert(LDS <= 160 * 1024, "gfx950 LDS is 160 KiB per workgroup");
+  static_assert(LDS * OCC <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
   // kernel stages per 128-K stage of the block-scale layouts
   static constexpr int SPL = 128 / C::KSTAGE;
   static_assert(!C::SCALED || C::NV || (SPL == 2 && C::STEPS == 1) || (SPL == 1 && C::STEPS == 2),
@@ -237,7 +242,8 @@ __device__ __forceinline__ void boundary_hint() {
 }
 
 template <int FMT, int BM, int LAYER>
-__global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) k_gemm(const GemmArgs p) {
+__global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
+    __attribute__((amdgpu_waves_per_eu((TileGeom<FMT, BM>::OCC), (TileGeom<FMT, BM>::OCC)))) k_gemm(const GemmArgs p) {
   using G = TileGeom<FMT, BM>;
   using C = typename G::C;
   using FA = typename Frag<FMT>::A;
@@ -476,14 +482,23 @@ __global__ void __launch_bounds__(GEMM_THREADS, 1) __attribute__((amdgpu_waves_p
   // buffer that is not read again (stage indices clamped), which keeps the
   // copy count per stage fixed for the vmcnt bookkeeping.
   const bool chain = nstages >= G::NBUF - 1;
-  const int u0 = xcd * per_xcd + xj;
+  // work unit of round r: in a full round each XCD takes a contiguous run
+  // (M blocks sharing a weight block meet in one L2); a partial last round
+  // is dealt out across the XCDs in turn, so a small launch uses them all
+  const int NW = (int)gridDim.x;
+  auto unit = [&](int r) __attribute__((always_inline)) -> int {
+    const int base = r * NW;
+    return base + NW <= total ? base + xcd * per_xcd + xj : base + (int)blockIdx.x;
+  };
+  const int u0 = unit(0);
   TileCtx ta, tb;
   int cur = 0;           // LDS buffer of the current stage
   bool primed = false;   // the current tile's first NBUF-1 stages are issued
   if (u0 < total) ta = make_tile(u0);
-  for (int u = u0; u < total; u += gridDim.x) {
-    const bool has_next = u + (int)gridDim.x < total;
-    if (has_next) tb = make_tile(u + gridDim.x);
+  for (int r = 0; unit(r) < total; ++r) {
+    const int un = unit(r + 1);
+    const bool has_next = un < total;
+    if (has_next) tb = make_tile(un);
     const bool chain_next = chain && has_next;
     lds_barrier();        // every wave is done with the previous tile's LDS
     // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
@@ -704,10 +719,13 @@ hipError_t gemm_init(int /*device*/) {
 template <int FMT, int BM>
 static hipError_t launch_fmt_bm(int layer, const GemmArgs& a, int grid, hipStream_t st) {
   constexpr int lds = TileGeom<FMT, BM>::LDS;
+  // the persistent grid: OCC workgroups per CU (grid is a multiple of 8, so
+  // the XCD round-robin of workgroups stays exact)
+  const int g = grid * TileGeom<FMT, BM>::OCC;
   if (layer == 1)
-    hipLaunchKernelGGL((k_gemm<FMT, BM, 1>), dim3(grid), dim3(GEMM_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<FMT, BM, 1>), dim3(g), dim3(GEMM_THREADS), lds, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, BM, 2>), dim3(grid), dim3(GEMM_THREADS), lds, st, a);
+    hipLaunchKernelGGL((k_gemm<FMT, BM, 2>), dim3(g), dim3(GEMM_THREADS), lds, st, a);
   return hipGetLastError();
 }
 
