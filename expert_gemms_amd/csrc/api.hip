@@ -70,10 +70,12 @@ struct Workspace {
   int32_t* slot_row;
   int32_t* tile_expert;
   uint8_t* xq;        // dispatch-quantised x codes
-  uint8_t* xq_sf;     // its block scales
+  uint8_t* xq_sf;     // its block scales, [T, H / block]
+  uint8_t* a1_sf;     // the same in sorted-row planes (one per K block)
+  int64_t sf_plane;   // bytes per scale plane (a1_sf, a2_sf)
   float* x_tok;       // NVFP4 per-token scale
   uint8_t* a2;        // L2 input codes
-  uint8_t* a2_sf;     // L2 input block scales
+  uint8_t* a2_sf;     // L2 input block scales, planes of sorted rows
   float* o;           // L2 output rows per slot
   uint16_t* xw;       // BF16 input rows scaled by their routing weight
   size_t bytes;
@@ -91,19 +93,24 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   w.sorted_slot = (int32_t*)take(M * 4);
   w.slot_row = (int32_t*)take(S * 4);
   w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
-  w.xq = w.xq_sf = w.a2 = w.a2_sf = nullptr;
+  w.xq = w.xq_sf = w.a1_sf = w.a2 = w.a2_sf = nullptr;
   w.x_tok = nullptr;
+  // a scale plane holds every sorted row plus 256 bytes, so a tile's
+  // 256-byte plane copy from its first row stays inside
+  w.sf_plane = (M + 256 + 255) / 256 * 256;
   if (fmt == F_MXFP8 || fmt == F_MXFP4) {
     w.xq = take(T * H);
     w.xq_sf = take(T * H / 32);
+    w.a1_sf = take(H / 32 * w.sf_plane);
     w.a2 = take(M * I);
-    w.a2_sf = take(M * I / 32);
+    w.a2_sf = take(I / 32 * w.sf_plane);
   } else if (fmt == F_NVFP4) {
     w.xq = take(T * H / 2);
     w.xq_sf = take(T * H / 16);
+    w.a1_sf = take(H / 16 * w.sf_plane);
     w.x_tok = (float*)take(T * 4);
     w.a2 = take(M * I / 2);
-    w.a2_sf = take(M * I / 16);
+    w.a2_sf = take(I / 16 * w.sf_plane);
   } else {
     w.a2 = take(M * I * 2);
   }
@@ -394,6 +401,15 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   mark(2 * MOE_STEP_DISPATCH);
   launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts, w.offsets,
                   w.sorted_slot, w.slot_row, w.tile_expert, w.meta, s);
+  const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
+  const int64_t grp = nv ? 16 : 32;          // elements per block scale
+  if (scaled) {
+    // the dispatch-quantised x scales in the sorted rows' plane layout
+    // (padding rows: scale 1)
+    const int64_t M = T * kk + (int64_t)E * (bm - 1);
+    launch_gather_sf(w.sorted_slot, w.offsets, E, (int)kk, w.xq_sf, (int)(H / grp), w.sf_plane, M,
+                     nv ? 0x38 : 127, w.a1_sf, s);
+  }
   mark(2 * MOE_STEP_DISPATCH + 1);
   const int grid = (d->cus >= 8 ? d->cus : 8) / 8 * 8;
 
@@ -401,16 +417,14 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   const int64_t ebytes = fmt == MOE_FMT_BF16 ? 2 : 1;  // bytes per element (codes); FP4 below
-  const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
-  const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (fmt == MOE_FMT_BF16) {
     g.a = (const uint8_t*)xin;
     g.a_ld = H * 2;
   } else {
     g.a = w.xq;
     g.a_ld = nv ? H / 2 : H;
-    g.a_sf = w.xq_sf;
-    g.a_sf_ld = H / grp;
+    g.a_sf = w.a1_sf;
+    g.a_sf_ld = w.sf_plane;
     g.a_tok = w.x_tok;
   }
   g.w = (const uint8_t*)w13_k;
@@ -429,7 +443,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.c = w.a2;
   g.c_sf = w.a2_sf;
   g.c_ld = fmt == MOE_FMT_BF16 ? I * 2 : (nv ? I / 2 : I);
-  g.c_sf_ld = I / grp;
+  g.c_sf_ld = w.sf_plane;
   g.inter = (int)I;
   g.has_clamp = a.has_clamp;
   g.clamp = a.clamp;
@@ -447,7 +461,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g2.a = w.a2;
   g2.a_ld = g.c_ld;
   g2.a_sf = w.a2_sf;
-  g2.a_sf_ld = I / grp;
+  g2.a_sf_ld = w.sf_plane;
   g2.a_tok = nullptr;
   g2.w = (const uint8_t*)w2_k;
   g2.w_sf = (const uint8_t*)w2_sf_k;

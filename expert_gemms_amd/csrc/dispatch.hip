@@ -141,4 +141,53 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
                      n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta);
 }
 
+// Block scales of the L1 A operand in the GEMM's layout: one plane per
+// K block (plane kb holds the scale of every sorted row, row-contiguous), so
+// a tile's scales for one K block are BLOCK_M consecutive bytes.  Row m of
+// the sorted order takes the scale row of token sorted_slot[m] / kk; a
+// padding row, and the rows from offsets[E] to the next multiple of 4, take
+// `fill`.  A thread takes 4 rows and 8 planes (blockIdx.y: the plane
+// group) and stores a dword of 4 rows per plane (256 consecutive bytes per
+// wave).
+__global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ sorted_slot,
+                                                   const int32_t* __restrict__ offsets, int E, int kk,
+                                                   const uint8_t* __restrict__ x_sf, int sf_ld, int64_t plane,
+                                                   uint8_t fill, uint8_t* __restrict__ out) {
+  const int m = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int M = offsets[E];
+  if (m >= M) return;
+  const uint8_t* src[4];
+  bool real[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sl = m + i < M ? sorted_slot[m + i] : -1;
+    real[i] = sl >= 0;
+    src[i] = x_sf + (int64_t)(real[i] ? sl / kk : 0) * sf_ld;
+  }
+  {
+    const int kb = blockIdx.y * 8;
+    uint2 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *(const uint2*)(src[i] + kb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b = real[i] ? ((j < 4 ? v[i].x : v[i].y) >> (8 * (j & 3))) & 0xFF : fill;
+        word |= b << (8 * i);
+      }
+      *(uint32_t*)(out + (int64_t)(kb + j) * plane + m) = word;
+    }
+  }
+}
+
+void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E, int kk, const uint8_t* x_sf,
+                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((max_rows + 1023) / 1024);
+  if (blocks == 0 || sf_ld < 8) return;
+  hipLaunchKernelGGL(k_gather_sf, dim3(blocks, (unsigned)(sf_ld / 8)), dim3(256), 0, stream, sorted_slot, offsets, E, kk, x_sf, sf_ld,
+                     plane, fill, out);
+}
+
 }  // namespace moe

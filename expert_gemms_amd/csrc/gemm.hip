@@ -99,11 +99,14 @@ struct TileGeom {
   // every wave issues at least one A copy (rows wrap modulo BM)
   static constexpr int A_STAGE = BM * C::A_ROW < 4096 ? 4096 : BM * C::A_ROW;
   static constexpr int B_STAGE = GEMM_BN * C::B_ROW;
-  // every wave copies 64 rows of A scales (rows wrap modulo BM; NVFP4: two
-  // halves of 4 bytes) and its own B scales, so the copy code has no wave
-  // branches
+  // A scales: 256 bytes (one K block's plane from the tile's first row on)
+  // per copy, one copy per wave (MX: a 128-K stage's 4 blocks, a 64-K
+  // stage's 2 blocks twice), two for NVFP4 (8 blocks); B scales: every wave
+  // copies its own, so the copy code has no wave branches
   static constexpr int A_SF_STAGE = C::SCALED ? (C::NV ? 2 : 1) * 4 * 256 : 0;
-  static constexpr int B_SF_STAGE = C::SCALED ? 4 * 1024 : 0;
+  // B scales: MX 1 KiB per stage (the 8 column blocks' 128 bytes, a quarter
+  // per wave), NVFP4 1 KiB per wave (its column blocks)
+  static constexpr int B_SF_STAGE = C::SCALED ? (C::NV ? 4 : 1) * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
   // LDS stage buffers: the format's ring depth (or as many as fit) for the
   // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
@@ -275,7 +278,6 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     int s0;                 // first K stage of the work unit
     int ks;                 // its K split
     int64_t a_off[G::A_INSTR];
-    int64_t asf_off;
     const uint8_t* wexp;
     const uint8_t* wsf;
   };
@@ -323,18 +325,6 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       }
       t.a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
     }
-    t.asf_off = 0;
-    if constexpr (C::SCALED) {
-      const int r = (w * 64 + lane) % BM;
-      int64_t row;
-      if (LAYER == 1) {
-        const int sl = p.sorted_slot[t.m0 + r];
-        row = sl >= 0 ? sl / p.kk : 0;
-      } else {
-        row = t.m0 + r;
-      }
-      t.asf_off = row * p.a_sf_ld;
-    }
     t.wexp = p.w + (int64_t)e * p.w_expert_bytes;
     t.wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
     return t;
@@ -358,19 +348,25 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
                            (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
       g2lds16(src, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
-      // A scales: this stage's 4 UE8M0 bytes of rows w*64 .. w*64+63 (mod BM)
-      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + ((t.s0 + s) / G::SPL) * 4,
+      // A scales: K block w % (blocks per stage) of this stage, the plane's
+      // bytes of rows m0 .. m0+255 (rows past the tile are not read)
+      constexpr int NBLK = C::KSTAGE / 32;
+      const int64_t blk = (int64_t)(t.s0 + s) * NBLK + w % NBLK;
+      __builtin_amdgcn_global_load_lds(p.a_sf + blk * p.a_sf_ld + t.m0 + lane * 4,
                                        (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
     } else if constexpr (!C::NV) {
-      // B scales: [stage][32-row block][64 lanes x 2 K-steps], one copy per wave
-      const uint8_t* src = t.wsf + ((int64_t)((t.s0 + s) / G::SPL) * (p.N / 32) + t.nb * 8 + (lane >> 3)) * 128 + (lane & 7) * 16;
-      g2lds16(src, st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 1024);
+      // B scales: [layout stage][32-row block][64 lanes x 2 K-steps]; wave w
+      // copies column blocks 2w and 2w + 1 (256 contiguous bytes)
+      const uint8_t* src = t.wsf + ((int64_t)((t.s0 + s) / G::SPL) * (p.N / 32) + t.nb * 8 + 2 * w) * 128 + lane * 4;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 256), 4, 0,
+                                       0);
     } else if constexpr (c < SC + 2) {
-      // NVFP4 A scales: this stage's 8 E4M3 bytes of rows w*64 .. (mod BM),
-      // as two halves of 4 (64-K group 0, group 1)
+      // NVFP4 A scales: K blocks w and w + 4 of this stage's 8, the planes'
+      // bytes of rows m0 .. m0+255
       constexpr int h = c - SC;
-      __builtin_amdgcn_global_load_lds(p.a_sf + t.asf_off + (t.s0 + s) * 8 + 4 * h,
-                                       (lds_void*)(st + G::A_STAGE + G::B_STAGE + 1024 * h + w * 256), 4, 0, 0);
+      const int64_t blk = (int64_t)(t.s0 + s) * 8 + w + 4 * h;
+      __builtin_amdgcn_global_load_lds(p.a_sf + blk * p.a_sf_ld + t.m0 + lane * 4,
+                                       (lds_void*)(st + G::A_STAGE + G::B_STAGE + (w + 4 * h) * 256), 4, 0, 0);
     } else {
       // NVFP4 B scales of this wave's TN blocks: [stage][32-row block][64 lanes x 4]
       const int byte = (lane * 16) % (TN * 256);
@@ -386,10 +382,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
 
   f32x16 acc[TM][TN];   // the tile's accumulators (AGPRs)
   // Block scales of a stage (in buffer st) of parity PAR.  MX: for each
-  // K-step, the one UE8M0 byte each lane hands its scaled MFMA: K-step kl of
-  // the 128-K layout stage (kl = the K-step, or for 64-K stages the stage
-  // parity) takes A block 2*kl + g and B byte kl; read as bytes so no VALU
-  // work waits on the LDS read.  NVFP4: dwords of 4 E4M3 scales.
+  // K-step, the one UE8M0 byte each lane hands its scaled MFMA: the A byte
+  // of the lane's row in K block 2 * (K-step) + g of the stage, and B byte
+  // kl of the lane's 128-K layout stage (kl = the K-step, or for 64-K stages
+  // the stage parity); read as bytes so no VALU work waits on the LDS read.
+  // NVFP4: two E4M3 A scales per row and 64-K group, a dword of four B
+  // scales per column block.
   auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[SB_N])
       __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;
@@ -400,14 +398,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       for (int tm = 0; tm < TM; ++tm) {
         const int r = wm * TM * 32 + tm * 32 + l32;
         if constexpr (C::NV) {
-          sa[tm] = *(const uint32_t*)(Asf + r * 4);
-          sa[TM + tm] = *(const uint32_t*)(Asf + 1024 + r * 4);
-        } else {
+          // 64-K group ks: lane group g takes K blocks 4ks + 2g and + 1
 #pragma unroll
-          for (int ks = 0; ks < C::STEPS; ++ks) {
-            const int kl = C::STEPS == 1 ? PAR : ks;
-            sa[ks * TM + tm] = Asf[r * 4 + 2 * kl + g];
-          }
+          for (int ks = 0; ks < 2; ++ks)
+            sa[ks * TM + tm] = (uint32_t)Asf[(4 * ks + 2 * g) * 256 + r] |
+                               ((uint32_t)Asf[(4 * ks + 2 * g + 1) * 256 + r] << 8);
+        } else {
+          // K-step ks takes K block 2ks + g of the stage
+#pragma unroll
+          for (int ks = 0; ks < C::STEPS; ++ks) sa[ks * TM + tm] = Asf[(2 * ks + g) * 256 + r];
         }
       }
 #pragma unroll
@@ -435,7 +434,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
         NvScale ssa[TM], ssb[TN];
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * (2 * g + h))) & 0xFF);
+        for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * h)) & 0xFF);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) ssb[tn] = nv_scale((sb[tn] >> (8 * (2 * ks + h))) & 0xFF);
 #pragma unroll
@@ -644,7 +643,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
               }
               const uint32_t qn = (uint32_t)shfl_xor((int)q, 1);
               if ((l32 & 1) == 0) p.c[(int64_t)row * p.c_ld + (icol >> 1)] = (uint8_t)(q | (qn << 4));
-              if ((l32 & 15) == 0) p.c_sf[(int64_t)row * p.c_sf_ld + (icol >> 4)] = (uint8_t)bs;
+              if ((l32 & 15) == 0) p.c_sf[(int64_t)(icol >> 4) * p.c_sf_ld + row] = (uint8_t)bs;
             } else if constexpr (FMT == F_BF16) {
               ((uint16_t*)(p.c + (int64_t)row * p.c_ld))[icol] = bf16_rne(a);
             } else {
@@ -658,7 +657,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
                 q = e4m3_encode(__builtin_ldexpf(a, 127 - c));
               }
               p.c[(int64_t)row * p.c_ld + icol] = (uint8_t)q;
-              if (l32 == 0) p.c_sf[(int64_t)row * p.c_sf_ld + (icol >> 5)] = (uint8_t)c;
+              if (l32 == 0) p.c_sf[(int64_t)(icol >> 5) * p.c_sf_ld + row] = (uint8_t)c;
             }
           }
           __builtin_amdgcn_sched_barrier(0);

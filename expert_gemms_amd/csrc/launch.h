@@ -16,10 +16,12 @@ struct GemmArgs {
   // A operand: rows of x (L1, gathered through sorted_slot / k') or of the
   // L2 input (L2, already in sorted order).
   const uint8_t* a;        // element codes (BF16 / E4M3 / packed E2M1)
-  const uint8_t* a_sf;     // block scales (UE8M0 or E4M3), NULL for BF16
+  const uint8_t* a_sf;     // block scales (UE8M0 or E4M3), NULL for BF16: one
+                           // plane per K block, a byte per sorted row
   const float* a_tok;      // NVFP4 L1: per-token global scale
   int64_t a_ld;            // bytes per A row
-  int64_t a_sf_ld;         // bytes per A scale row
+  int64_t a_sf_ld;         // bytes per A-scale plane (a multiple of 256; rows
+                           // up to the last tile's start + 255 are readable)
   // B operand: kernel-layout weights of all local experts.
   const uint8_t* w;
   const uint8_t* w_sf;
@@ -36,7 +38,7 @@ struct GemmArgs {
   // L1 epilogue: activation + L2-input quantisation into (c, c_sf)
   uint8_t* c;
   uint8_t* c_sf;
-  int64_t c_ld, c_sf_ld;
+  int64_t c_ld, c_sf_ld;   // c_sf: planes of c_sf_ld bytes, as a_sf
   int inter;
   int has_clamp;
   float clamp, alpha, beta;
@@ -61,6 +63,11 @@ hipError_t gemm_init(int device);
 // post-expert RMSNorm.
 void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
                     int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream);
+// L1 A-operand block scales x_sf [T, sf_ld] -> block-major planes of the
+// sorted rows: out[kb * plane + m] (rows m < offsets[E]).
+void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E, int kk, const uint8_t* x_sf,
+                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, hipStream_t stream);
+
 void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream);
 
 void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13_sf,
