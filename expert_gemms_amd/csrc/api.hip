@@ -76,13 +76,14 @@ struct Workspace {
   float* x_tok;       // NVFP4 per-token scale
   uint8_t* a2;        // L2 input codes
   uint8_t* a2_sf;     // L2 input block scales, planes of sorted rows
+  float* p1;          // K parts of a split L1 GEMM, float32 [ksplit1, S, 2I]
   float* o;           // L2 output rows per slot
   uint16_t* xw;       // BF16 input rows scaled by their routing weight
   size_t bytes;
 };
 
 Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t n_sh, int64_t k, int64_t bm,
-               int64_t ksplit, uint8_t* base) {
+               int64_t ksplit, int64_t ksplit1, uint8_t* base) {
   const int64_t E = n_loc + n_sh, S = T * (k + n_sh), M = S + E * (bm - 1);
   Workspace w;
   size_t off = 0;
@@ -115,6 +116,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
     w.a2 = take(M * I * 2);
   }
   w.o = (float*)take(S * H * 4 * ksplit);
+  w.p1 = ksplit1 > 1 ? (float*)take(S * 2 * I * 4 * ksplit1) : nullptr;
   w.xw = (uint16_t*)take(T * H * 2);
   w.bytes = off;
   return w;
@@ -171,9 +173,8 @@ constexpr int SPLIT_RULE_CUS = 256;
 // K into ks parts (each part's float32 result in its own buffer, added by the
 // combine) fills it at the price of (ks - 1) extra O writes and reads.  The
 // estimate takes the tile time from a nominal per-format MFMA rate; ks must
-// divide the stage count (and leave an even count per part where a stage is
-// half of a 128-K block-scale stage).  The choice does not depend on the
-// BLOCK_M a caller passes, so every BLOCK_M sums in the same order.
+// divide the stage count.  The choice does not depend on the BLOCK_M a caller
+// passes, so every BLOCK_M sums in the same order.
 int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int k, int cus) {
   if (T <= 0 || cus <= 0) return 1;
   const int bm = block_m_rule((int)T, n_loc, n_sh, k, fmt);
@@ -191,6 +192,35 @@ int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
     if (nst % ks) continue;
     const double t = std::ceil(tiles * ks / cus) * t_tile / ks + (ks - 1) * S * (double)H * 8.0 / 5.0e12;
     if (ks == 1 || t < 0.97 * best_t) {   // a split must win by 3 %
+      best = ks;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+// K splits of the L1 GEMM, for launches with few tiles (decode batches):
+// when the tiles leave work slots idle (two per CU for the small tiles such
+// launches use), each tile's K is cut into ks parts that run as separate work
+// units; the float32 parts (per slot) are summed by the finish kernel before
+// the activation.  Counted in tile rounds, with a twentieth of a round per
+// extra part for the finish and the parts' traffic.  ks divides the stage
+// count; BLOCK_M-independent like the L2 rule.
+int l1_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int k, int cus) {
+  if (T <= 0 || cus <= 0) return 1;
+  const int bm = block_m_rule((int)T, n_loc, n_sh, k, fmt);
+  const double mtiles = n_loc * expected_padded((double)T * k / n_loc, bm) / bm +
+                        n_sh * (double)((T + bm - 1) / bm);
+  const double tiles = std::max(1.0, mtiles * (double)(2 * I / GEMM_BN));
+  const double slots = (bm <= 64 ? 2.0 : 1.0) * cus;
+  const int kst = fmt == MOE_FMT_BF16 ? 32 : 128;
+  const int64_t nst = H / kst;
+  int best = 1;
+  double best_t = 0.0;
+  for (int ks = 1; ks <= 4; ++ks) {
+    if (nst % ks) continue;
+    const double t = std::ceil(tiles * ks / slots) / ks + 0.05 * (ks - 1);
+    if (ks == 1 || t < best_t) {
       best = ks;
       best_t = t;
     }
@@ -235,7 +265,8 @@ size_t moe_workspace_bytes(moe_format_t fmt, int max_tokens, int hidden, int int
   if (block_m == 0) block_m = 256;
   if (block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return 0;
   const int ks = l2_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, ks, nullptr).bytes;
+  const int ks1 = l1_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, ks, ks1, nullptr).bytes;
 }
 
 int moe_transform_weights(moe_format_t fmt, int num_experts, int hidden, int inter, const void* w13,
@@ -372,14 +403,16 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
   const int E = num_local_experts + num_shared;
   int ks = l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, nullptr).bytes > workspace_bytes) ks = 1;
-  if (plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, nullptr).bytes > workspace_bytes)
-    return MOE_E_WORKSPACE;
+  int ks1 = l1_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  auto need = [&]() { return plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, nullptr).bytes; };
+  if (need() > workspace_bytes) ks1 = 1;
+  if (need() > workspace_bytes) ks = 1;
+  if (need() > workspace_bytes) return MOE_E_WORKSPACE;
   DeviceInfo* d;
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, (uint8_t*)workspace);
+  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, (uint8_t*)workspace);
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };
@@ -450,10 +483,13 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.alpha = a.alpha;
   g.beta = a.beta;
   g.l2_scale = l2_activation_scale;
-  g.ksplit = 1;
+  g.ksplit = ks1;
+  g.o = w.p1;
+  g.o_split = T * kk * 2 * I;
   mark(2 * MOE_STEP_L1);
   hipError_t e = launch_gemm(fmt, 1, bm, g, grid, s);
   if (e != hipSuccess) return hip_status(e);
+  if (ks1 > 1) launch_l1_finish(fmt, g, w.slot_row, w.tile_expert, bm, (int)(T * kk), s);
   mark(2 * MOE_STEP_L1 + 1);
 
   // a6: L2 GEMM

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "l2input.h"
 #include "launch.h"
 
 namespace moe {
@@ -79,15 +80,6 @@ template <int FMT, int BM> struct Cfg : FmtCfg<FMT> {};
 template <> struct Cfg<F_MXFP8, 256> : FmtCfg<F_MXFP8> {
   static constexpr int KSTAGE = 64, A_ROW = 64, B_ROW = 64, STEPS = 1, NBUF = 4;
 };
-
-__device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
-  if (p.has_clamp) {
-    g = __builtin_fminf(g, p.clamp);
-    u = __builtin_fminf(__builtin_fmaxf(u, -p.clamp), p.clamp);
-  }
-  float s = __builtin_amdgcn_rcpf(1.0f + __expf(-p.alpha * g));
-  return g * s * (u + p.beta);
-}
 
 template <int FMT, int BM>
 struct TileGeom {
@@ -610,7 +602,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
 
     // ---- epilogue.  Accumulator element v of lane l is row
     // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32 of its 32x32 tile.
-    if constexpr (LAYER == 1) {
+    // L1 with K unsplit: activation and L2-input quantisation here.  L2, and
+    // L1 with K split: float32 rows per slot (L1: raw accumulators in the
+    // kernel's column order, summed and activated by k_l1_finish).
+    if (LAYER == 1 && p.ksplit == 1) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -627,45 +622,14 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
               gv *= alpha;
               uv *= alpha;
             }
-            const float a = act_swiglu(gv, uv, p);
-            if constexpr (C::NV) {
-              // NVFP4 L2 input with the one global scale g2: E4M3 scale per 16
-              // intermediate columns (16 lanes), E2M1 codes two per byte
-#pragma clang fp contract(off)
-              const float amax = group_max<4>(__builtin_fabsf(a));
-              const float six_g = 6.0f * p.l2_scale;
-              const uint32_t bs = e4m3_encode(amax / six_g);
-              const float bsv = e4m3_decode(bs);
-              uint32_t q = 0;
-              if (bsv != 0.0f) {
-                const float r = 1.0f / (bsv * p.l2_scale);
-                q = e2m1_encode(a * r);
-              }
-              const uint32_t qn = (uint32_t)shfl_xor((int)q, 1);
-              if ((l32 & 1) == 0) p.c[(int64_t)row * p.c_ld + (icol >> 1)] = (uint8_t)(q | (qn << 4));
-              if ((l32 & 15) == 0) p.c_sf[(int64_t)(icol >> 4) * p.c_sf_ld + row] = (uint8_t)bs;
-            } else if constexpr (FMT == F_BF16) {
-              ((uint16_t*)(p.c + (int64_t)row * p.c_ld))[icol] = bf16_rne(a);
-            } else {
-              // MXFP8 L2 input: one UE8M0 scale per 32 intermediate columns,
-              // which are exactly the 32 lanes of this half-wave.
-              const float amax = group_max<5>(__builtin_fabsf(a));
-              uint32_t q = 0;
-              int c = 0;
-              if (amax > 0.0f) {
-                c = mx_scale_code<false>(amax);
-                q = e4m3_encode(__builtin_ldexpf(a, 127 - c));
-              }
-              p.c[(int64_t)row * p.c_ld + icol] = (uint8_t)q;
-              if (l32 == 0) p.c_sf[(int64_t)(icol >> 5) * p.c_sf_ld + row] = (uint8_t)c;
-            }
+            store_l2_input<FMT>(act_swiglu(gv, uv, p), row, icol, l32, p);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      // NVFP4: w2's expert scale times the L2 input's global scale
-      const float alpha2 = C::NV ? p.w_gs[e] * p.l2_scale : 1.0f;
+      // NVFP4 L2: w2's expert scale times the L2 input's global scale
+      const float alpha2 = C::NV && LAYER == 2 ? p.w_gs[e] * p.l2_scale : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -675,13 +639,52 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           if (slot < 0) continue;
           float* orow = p.o + ta.ks * p.o_split + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
+          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
         }
       }
     }
     if (has_next) ta = tb;
   }
   wait_vmcnt0();   // no LDS-DMA copy outlives the workgroup
+}
+
+// Finish of a K-split L1 GEMM: per slot, the float32 parts of its gate and up
+// columns summed in part order (NVFP4: times the token and expert scales, as
+// the unsplit epilogue does), then the same activation and L2-input
+// quantisation as the unsplit epilogue, into the slot's sorted row.  One wave
+// per (slot, 64 intermediate columns); a dropped slot has no row.
+template <int FMT>
+__global__ void __launch_bounds__(64) k_l1_finish(const GemmArgs p, const int32_t* __restrict__ slot_row,
+                                                  const int32_t* __restrict__ tile_expert, int bm) {
+  const int s = blockIdx.x;
+  const int m = slot_row[s];
+  if (m < 0) return;
+  const int lane = threadIdx.x, l32 = lane & 31;
+  const int icol = blockIdx.y * 64 + lane;
+  const int nc = (icol >> 5) * 64 + (icol & 31);   // gate column; up is 32 further
+  float g = 0.0f, u = 0.0f;
+  for (int ks = 0; ks < p.ksplit; ++ks) {
+    const float* row = p.o + ks * p.o_split + (int64_t)s * p.N;
+    g += row[nc];
+    u += row[nc + 32];
+  }
+  if constexpr (FMT == F_NVFP4) {
+    const float alpha = p.a_tok[s / p.kk] * p.w_gs[tile_expert[m / bm]];
+    g *= alpha;
+    u *= alpha;
+  }
+  store_l2_input<FMT>(act_swiglu(g, u, p), m, icol, l32, p);
+}
+
+void launch_l1_finish(int fmt, const GemmArgs& a, const int32_t* slot_row, const int32_t* tile_expert, int bm,
+                      int S, hipStream_t st) {
+  const dim3 grid((unsigned)S, (unsigned)(a.inter / 64));
+  switch (fmt) {
+    case F_BF16: hipLaunchKernelGGL(k_l1_finish<F_BF16>, grid, dim3(64), 0, st, a, slot_row, tile_expert, bm); break;
+    case F_MXFP8: hipLaunchKernelGGL(k_l1_finish<F_MXFP8>, grid, dim3(64), 0, st, a, slot_row, tile_expert, bm); break;
+    case F_MXFP4: hipLaunchKernelGGL(k_l1_finish<F_MXFP4>, grid, dim3(64), 0, st, a, slot_row, tile_expert, bm); break;
+    default: hipLaunchKernelGGL(k_l1_finish<F_NVFP4>, grid, dim3(64), 0, st, a, slot_row, tile_expert, bm); break;
+  }
 }
 
 // ------------------------------------------------------------------ host side

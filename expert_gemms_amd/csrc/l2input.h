@@ -1,0 +1,63 @@
+// The gated activation and the quantisation of the L2 input, shared by the L1
+// GEMM epilogue and the kernel that finishes a K-split L1 GEMM, so both
+// write identical codes for identical activations.
+//
+// Activation (MegaMoEActivation on the DeepGEMM MegaMoE experts page): with a
+// clamp c, gate <- min(gate, c) and up <- clamp(up, -c, c); then
+// gate * sigmoid(alpha * gate) * (up + beta), float32 with the hardware exp
+// and reciprocal.  L2-input quantisation (the per-group quantisation between
+// the two GEMMs in the "fused_moe" page's DeepGemmExperts.apply): BF16 RNE;
+// MXFP8 one UE8M0 scale per 32 intermediate columns; NVFP4 one E4M3 scale
+// per 16 columns with the one global scale g2, E2M1 codes two per byte.
+// Scales go to planes of one byte per sorted row (plane stride c_sf_ld).
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+__device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
+  if (p.has_clamp) {
+    g = __builtin_fminf(g, p.clamp);
+    u = __builtin_fminf(__builtin_fmaxf(u, -p.clamp), p.clamp);
+  }
+  float s = __builtin_amdgcn_rcpf(1.0f + __expf(-p.alpha * g));
+  return g * s * (u + p.beta);
+}
+
+// Activation value a of sorted row `row`, intermediate column icol.  The 32
+// lanes of a half-wave hold 32 consecutive columns (icol % 32 == l32) of one
+// row: the MX scale group is the half-wave, the NVFP4 group 16 lanes.
+template <int FMT>
+__device__ __forceinline__ void store_l2_input(float a, int64_t row, int icol, int l32, const GemmArgs& p) {
+  if constexpr (FMT == F_NVFP4) {
+#pragma clang fp contract(off)
+    const float amax = group_max<4>(__builtin_fabsf(a));
+    const float six_g = 6.0f * p.l2_scale;
+    const uint32_t bs = e4m3_encode(amax / six_g);
+    const float bsv = e4m3_decode(bs);
+    uint32_t q = 0;
+    if (bsv != 0.0f) {
+      const float r = 1.0f / (bsv * p.l2_scale);
+      q = e2m1_encode(a * r);
+    }
+    const uint32_t qn = (uint32_t)shfl_xor((int)q, 1);
+    if ((l32 & 1) == 0) p.c[row * p.c_ld + (icol >> 1)] = (uint8_t)(q | (qn << 4));
+    if ((l32 & 15) == 0) p.c_sf[(int64_t)(icol >> 4) * p.c_sf_ld + row] = (uint8_t)bs;
+  } else if constexpr (FMT == F_BF16) {
+    ((uint16_t*)(p.c + row * p.c_ld))[icol] = bf16_rne(a);
+  } else {
+    const float amax = group_max<5>(__builtin_fabsf(a));
+    uint32_t q = 0;
+    int c = 0;
+    if (amax > 0.0f) {
+      c = mx_scale_code<false>(amax);
+      q = e4m3_encode(__builtin_ldexpf(a, 127 - c));
+    }
+    p.c[row * p.c_ld + icol] = (uint8_t)q;
+    if (l32 == 0) p.c_sf[(int64_t)(icol >> 5) * p.c_sf_ld + row] = (uint8_t)c;
+  }
+}
+
+}  // namespace moe

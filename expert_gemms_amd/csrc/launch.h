@@ -43,10 +43,11 @@ struct GemmArgs {
   int has_clamp;
   float clamp, alpha, beta;
   float l2_scale;          // NVFP4 global scale of the L2 input
-  // L2 epilogue: float32 rows per slot [S, H]; with K split in ksplit parts
-  // (L2 only), part ks goes to o + ks * o_split
+  // float32 rows per slot [S, N]: the L2 output, and the parts of an L1
+  // whose K is split; with K split in ksplit parts, part ks goes to
+  // o + ks * o_split
   float* o;
-  int ksplit;              // 1 for L1
+  int ksplit;
   int64_t o_split;
 };
 
@@ -55,6 +56,11 @@ enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
                      int32_t* tile_expert, int32_t* meta, hipStream_t stream);
+
+// Sum of the K parts of a split L1 GEMM (a.o, a.ksplit, a.o_split), then its
+// activation and L2-input quantisation into (a.c, a.c_sf).
+void launch_l1_finish(int fmt, const GemmArgs& a, const int32_t* slot_row, const int32_t* tile_expert, int bm,
+                      int S, hipStream_t st);
 
 hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& args, int grid, hipStream_t stream);
 hipError_t gemm_init(int device);

@@ -235,3 +235,19 @@ def test_forward_norm_zero_centred_gain_folded_by_holder():
     again = layer.forward(xd, idd, wd, norm_gamma=g2.cuda(), norm_eps=1e-6)
     assert torch.equal(folded, again)
     assert torch.allclose(folded.float(), direct.float(), rtol=1e-2, atol=1e-2)
+
+
+# Decode-sized launches: few tiles, so the L1 GEMM's K is split into parts
+# summed by the finish kernel before the activation.
+DECODE_SMALL = {
+    f"{fmt}_decode": MoEConfig(f"{fmt}_decode", 60 + i, fmt, 3, 512, 256, 32, 4, routing="softmax_uniform")
+    for i, fmt in enumerate(["bf16", "mxfp8", "mxfp4", "nvfp4"])
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_SMALL))
+def test_forward_decode_split_l1(name):
+    cfg = DECODE_SMALL[name]
+    ys = [compare(cfg, block_m=bm) for bm in (32, 64, 128, 256)]
+    for bm, y in zip((64, 128, 256), ys[1:]):
+        assert np.array_equal(ys[0], y), bm
