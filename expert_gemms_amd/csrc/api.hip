@@ -203,9 +203,11 @@ int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
 // when the tiles leave work slots idle (two per CU for the small tiles such
 // launches use), each tile's K is cut into ks parts that run as separate work
 // units; the float32 parts (per slot) are summed by the finish kernel before
-// the activation.  Counted in tile rounds, with a twentieth of a round per
-// extra part for the finish and the parts' traffic.  ks divides the stage
-// count; BLOCK_M-independent like the L2 rule.
+// the activation.  A tile's time is its MFMA work at a nominal per-format
+// rate or the streaming of its weight block at the slot's share of 6 TB/s,
+// whichever is longer; a split pays the parts' write and read at 5 TB/s and
+// the finish launch, and must win by 3 %.  ks divides the stage count;
+// BLOCK_M-independent like the L2 rule.
 int l1_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int k, int cus) {
   if (T <= 0 || cus <= 0) return 1;
   const int bm = block_m_rule((int)T, n_loc, n_sh, k, fmt);
@@ -213,14 +215,19 @@ int l1_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
                         n_sh * (double)((T + bm - 1) / bm);
   const double tiles = std::max(1.0, mtiles * (double)(2 * I / GEMM_BN));
   const double slots = (bm <= 64 ? 2.0 : 1.0) * cus;
+  const double rate = (fmt == MOE_FMT_BF16 ? 1.0e15 : (fmt == MOE_FMT_NVFP4 ? 0.6e15 : 1.6e15)) / slots;
+  const double elem = fmt == MOE_FMT_BF16 ? 2.0 : (fmt == MOE_FMT_MXFP8 ? 1.0 : 0.5);
+  const double t_tile = std::max(2.0 * bm * GEMM_BN * (double)H / rate, GEMM_BN * (double)H * elem / (6.0e12 / slots));
+  const double S = (double)T * (k + n_sh);
   const int kst = fmt == MOE_FMT_BF16 ? 32 : 128;
   const int64_t nst = H / kst;
   int best = 1;
   double best_t = 0.0;
   for (int ks = 1; ks <= 4; ++ks) {
     if (nst % ks) continue;
-    const double t = std::ceil(tiles * ks / slots) / ks + 0.05 * (ks - 1);
-    if (ks == 1 || t < best_t) {
+    double t = std::ceil(tiles * ks / slots) * t_tile / ks;
+    if (ks > 1) t += ks * S * 2.0 * (double)I * 8.0 / 5.0e12 + 3.0e-6;
+    if (ks == 1 || t < 0.97 * best_t) {
       best = ks;
       best_t = t;
     }

@@ -100,15 +100,15 @@ struct TileGeom {
   // per wave), NVFP4 1 KiB per wave (its column blocks)
   static constexpr int B_SF_STAGE = C::SCALED ? (C::NV ? 4 : 1) * 1024 : 0;
   static constexpr int STAGE = A_STAGE + B_STAGE + A_SF_STAGE + B_SF_STAGE;
-  // LDS stage buffers: the format's ring depth (or as many as fit) for the
-  // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
-  // weight-streaming launches, whose stages are short and need more copies in
-  // flight.
   // workgroups per CU: two for the small tiles of weight-streaming launches
   // when three stage buffers each fit in half the LDS (while one workgroup
   // waits at a stage boundary the other computes or issues copies), else
   // one (the MFMA-bound tiles also need every register)
   static constexpr int OCC = BM <= 64 && 3 * STAGE + (C::NV ? 1024 : 0) <= 80 * 1024 ? 2 : 1;
+  // LDS stage buffers: the format's ring depth (or as many as fit) for the
+  // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
+  // weight-streaming launches, whose stages are short and need more copies in
+  // flight.
   static constexpr int NBUF_FIT = (160 * 1024 / OCC - (C::NV ? 1024 : 0)) / STAGE;
   static constexpr int NBUF = BM >= 128 ? (C::NBUF < NBUF_FIT ? C::NBUF : NBUF_FIT) : (NBUF_FIT < 8 ? NBUF_FIT : 8);
   static constexpr int ROWS_OFF = NBUF * STAGE;      // per-row epilogue scales (NVFP4)
@@ -236,6 +236,9 @@ __device__ __forceinline__ void boundary_hint() {
   boundary_mfma_hint<0, READS, MFMAS, VMEM>();
 }
 
+// LAYER 1: the L1 GEMM (A rows gathered from x through sorted_slot; the
+// activation and L2-input quantisation in the epilogue); 2: the L2 GEMM;
+// 3: one K part of a split L1 GEMM (gathered A rows, raw float32 output).
 template <int FMT, int BM, int LAYER>
 __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     __attribute__((amdgpu_waves_per_eu((TileGeom<FMT, BM>::OCC), (TileGeom<FMT, BM>::OCC)))) k_gemm(const GemmArgs p) {
@@ -309,7 +312,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
       const int r = rl % BM;
       int64_t row;
-      if (LAYER == 1) {
+      if (LAYER != 2) {
         const int sl = p.sorted_slot[t.m0 + r];
         row = sl >= 0 ? sl / p.kk : 0;
       } else {
@@ -494,7 +497,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     lds_barrier();        // every wave is done with the previous tile's LDS
     // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
     // (read after the K loop's barriers)
-    if constexpr (C::NV && LAYER == 1) {
+    if constexpr (C::NV && LAYER == 1) {   // (a K-split L1 leaves the scales to its finish)
       if (tid < BM) {
         const int sl = p.sorted_slot[ta.m0 + tid];
         ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[ta.e];
@@ -602,10 +605,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
 
     // ---- epilogue.  Accumulator element v of lane l is row
     // 8 * (v / 4) + 4 * (l / 32) + v % 4 and column l % 32 of its 32x32 tile.
-    // L1 with K unsplit: activation and L2-input quantisation here.  L2, and
-    // L1 with K split: float32 rows per slot (L1: raw accumulators in the
-    // kernel's column order, summed and activated by k_l1_finish).
-    if (LAYER == 1 && p.ksplit == 1) {
+    // L1: activation and L2-input quantisation here.  L2, and L1 with K
+    // split (LAYER 3): float32 rows per slot (LAYER 3: raw accumulators in
+    // the kernel's column order, summed and activated by k_l1_finish).
+    if constexpr (LAYER == 1) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -698,6 +701,7 @@ template <int FMT, int BM>
 static hipError_t init_fmt_bm() {
   hipError_t e = set_lds_attr<FMT, BM, 1>();
   if (e != hipSuccess) return e;
+  if ((e = set_lds_attr<FMT, BM, 3>()) != hipSuccess) return e;
   return set_lds_attr<FMT, BM, 2>();
 }
 
@@ -724,7 +728,9 @@ static hipError_t launch_fmt_bm(int layer, const GemmArgs& a, int grid, hipStrea
   // the persistent grid: OCC workgroups per CU (grid is a multiple of 8, so
   // the XCD round-robin of workgroups stays exact)
   const int g = grid * TileGeom<FMT, BM>::OCC;
-  if (layer == 1)
+  if (layer == 1 && a.ksplit > 1)
+    hipLaunchKernelGGL((k_gemm<FMT, BM, 3>), dim3(g), dim3(GEMM_THREADS), lds, st, a);
+  else if (layer == 1)
     hipLaunchKernelGGL((k_gemm<FMT, BM, 1>), dim3(g), dim3(GEMM_THREADS), lds, st, a);
   else
     hipLaunchKernelGGL((k_gemm<FMT, BM, 2>), dim3(g), dim3(GEMM_THREADS), lds, st, a);

@@ -155,3 +155,16 @@ def test_route_validates():
     assert lib.moe_route(4, 64, 8, f, None, 0, 1, 1, 1, float("inf"), None, f, f, None) == _lib.E_INVALID
     assert lib.moe_route(4, 64, 8, None, None, 0, 1, 1, 1, 1.0, None, f, f, None) == _lib.E_INVALID
     assert lib.moe_route(0, 64, 8, None, None, 0, 1, 1, 1, 1.0, None, None, None, None) == _lib.OK
+
+
+def test_l1_split_only_for_few_tiles():
+    """The float32 L1 parts of a K-split L1 GEMM are sized into the workspace
+    only when the split rule picks it: never for a prefill-sized launch (the
+    Mixtral-shaped layer's workspace stays well under the 3.7 GB that four
+    parts of 8192 x 28672 floats would add), always for a single decode
+    token (the parts of 8 slots add 8 * 3072 * 4 bytes per part)."""
+    big = moe.moe_workspace_bytes("bf16", 4096, 4096, 14336, 8, 0, 2, 0)
+    assert 0 < big < 1_000_000_000
+    one = moe.moe_workspace_bytes("mxfp4", 1, 4096, 1536, 128, 0, 8, 0)
+    two = moe.moe_workspace_bytes("mxfp4", 2, 4096, 1536, 128, 0, 8, 0)
+    assert one > 0 and two > one
