@@ -67,7 +67,8 @@ def copy_calibration(mb, reps=3):
     return 0
 
 
-KERNEL_SOURCES = ("expert_gemms_amd/csrc/gemm.hip", "expert_gemms_amd/csrc/common.h", "expert_gemms_amd/csrc/launch.h")
+KERNEL_SOURCES = ("expert_gemms_amd/csrc/gemm.hip", "expert_gemms_amd/csrc/common.h", "expert_gemms_amd/csrc/launch.h",
+                  "expert_gemms_amd/csrc/l2input.h")
 
 
 def kernel_sha256():
