@@ -633,12 +633,25 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     } else {
       // NVFP4 L2: w2's expert scale times the L2 input's global scale
       const float alpha2 = C::NV && LAYER == 2 ? p.w_gs[e] * p.l2_scale : 1.0f;
+      // the slots of the lane's 16 rows per row block, loaded together (four
+      // 16-byte loads each) before any store, so the loads share one wait
+      int slots[TM][16];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int4 s4 = *(const int4*)(p.sorted_slot + m0 + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
+          slots[tm][4 * q] = s4.x;
+          slots[tm][4 * q + 1] = s4.y;
+          slots[tm][4 * q + 2] = s4.z;
+          slots[tm][4 * q + 3] = s4.w;
+        }
+      }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-          const int slot = p.sorted_slot[row];
+          const int slot = slots[tm][v];
           if (slot < 0) continue;
           float* orow = p.o + ta.ks * p.o_split + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
 #pragma unroll
