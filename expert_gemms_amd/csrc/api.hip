@@ -73,7 +73,8 @@ struct Workspace {
   uint8_t* xq_sf;     // its block scales, [T, H / block]
   uint8_t* a1_sf;     // the same in sorted-row planes (one per K block)
   int64_t sf_plane;   // bytes per scale plane (a1_sf, a2_sf)
-  float* x_tok;       // NVFP4 per-token scale
+  float* x_tok;
+  float* row_tok;     // NVFP4: token scale of each sorted row       // NVFP4 per-token scale
   uint8_t* a2;        // L2 input codes
   uint8_t* a2_sf;     // L2 input block scales, planes of sorted rows
   float* p1;          // K parts of a split L1 GEMM, float32 [ksplit1, S, 2I]
@@ -95,7 +96,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   w.slot_row = (int32_t*)take(S * 4);
   w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
   w.xq = w.xq_sf = w.a1_sf = w.a2 = w.a2_sf = nullptr;
-  w.x_tok = nullptr;
+  w.x_tok = w.row_tok = nullptr;
   // a scale plane holds every sorted row plus 256 bytes, so a tile's
   // 256-byte plane copy from its first row stays inside
   w.sf_plane = (M + 256 + 255) / 256 * 256;
@@ -110,6 +111,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
     w.xq_sf = take(T * H / 16);
     w.a1_sf = take(H / 16 * w.sf_plane);
     w.x_tok = (float*)take(T * 4);
+    w.row_tok = (float*)take(M * 4);
     w.a2 = take(M * I / 2);
     w.a2_sf = take(I / 16 * w.sf_plane);
   } else {
@@ -448,7 +450,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
     // (padding rows: scale 1)
     const int64_t M = T * kk + (int64_t)E * (bm - 1);
     launch_gather_sf(w.sorted_slot, w.offsets, E, (int)kk, w.xq_sf, (int)(H / grp), w.sf_plane, M,
-                     nv ? 0x38 : 127, w.a1_sf, s);
+                     nv ? 0x38 : 127, w.a1_sf, nv ? w.x_tok : nullptr, w.row_tok, s);
   }
   mark(2 * MOE_STEP_DISPATCH + 1);
   const int grid = (d->cus >= 8 ? d->cus : 8) / 8 * 8;
@@ -477,6 +479,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.K = (int)H;
   g.sorted_slot = w.sorted_slot;
   g.offsets = w.offsets;
+  g.tile_expert = w.tile_expert;
+  g.row_scale = w.row_tok;
   g.meta = w.meta;
   g.num_experts = E;
   g.kk = (int)kk;

@@ -22,6 +22,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int WAVE = 64;
@@ -154,6 +155,27 @@ __device__ __forceinline__ int mx_scale_code(float amax) {
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Scalar (SMEM) loads of wave-uniform addresses, waited for on lgkmcnt.  A
+// kernel that keeps LDS-DMA copies in flight reads its metadata this way: the
+// use of a vector load makes the compiler wait for vmcnt(0), which would also
+// wait for every copy in flight.  (Loads only; nothing is written through the
+// scalar cache.)
+__device__ __forceinline__ int sload(const void* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ i32x8 sload8(const void* p) {
+  i32x8 v;
+  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ i32x16 sload16(const void* p) {
+  i32x16 v;
+  asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) {

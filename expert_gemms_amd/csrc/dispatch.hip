@@ -148,11 +148,13 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
 // padding row, and the rows from offsets[E] to the next multiple of 4, take
 // `fill`.  A thread takes 4 rows and 8 planes (blockIdx.y: the plane
 // group) and stores a dword of 4 rows per plane (256 consecutive bytes per
-// wave).
+// wave).  With a_tok (NVFP4), the first plane group also writes each row's
+// token scale to row_scale (1 for a padding row).
 __global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ sorted_slot,
                                                    const int32_t* __restrict__ offsets, int E, int kk,
                                                    const uint8_t* __restrict__ x_sf, int sf_ld, int64_t plane,
-                                                   uint8_t fill, uint8_t* __restrict__ out) {
+                                                   uint8_t fill, uint8_t* __restrict__ out,
+                                                   const float* __restrict__ a_tok, float* __restrict__ row_scale) {
   const int m = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int M = offsets[E];
   if (m >= M) return;
@@ -163,6 +165,7 @@ __global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ s
     const int sl = m + i < M ? sorted_slot[m + i] : -1;
     real[i] = sl >= 0;
     src[i] = x_sf + (int64_t)(real[i] ? sl / kk : 0) * sf_ld;
+    if (a_tok && blockIdx.y == 0 && m + i < M) row_scale[m + i] = real[i] ? a_tok[sl / kk] : 1.0f;
   }
   {
     const int kb = blockIdx.y * 8;
@@ -183,11 +186,12 @@ __global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ s
 }
 
 void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E, int kk, const uint8_t* x_sf,
-                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, hipStream_t stream) {
+                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, const float* a_tok,
+                      float* row_scale, hipStream_t stream) {
   const unsigned blocks = (unsigned)((max_rows + 1023) / 1024);
   if (blocks == 0 || sf_ld < 8) return;
   hipLaunchKernelGGL(k_gather_sf, dim3(blocks, (unsigned)(sf_ld / 8)), dim3(256), 0, stream, sorted_slot, offsets, E, kk, x_sf, sf_ld,
-                     plane, fill, out);
+                     plane, fill, out, a_tok, row_scale);
 }
 
 }  // namespace moe

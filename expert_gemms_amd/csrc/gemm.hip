@@ -104,15 +104,20 @@ struct TileGeom {
   // when three stage buffers each fit in half the LDS (while one workgroup
   // waits at a stage boundary the other computes or issues copies), else
   // one (the MFMA-bound tiles also need every register)
-  static constexpr int OCC = BM <= 64 && 3 * STAGE + (C::NV ? 1024 : 0) <= 80 * 1024 ? 2 : 1;
+  // per-row data of two tiles (the current one and the next), 4 bytes per row:
+  // NVFP4 L1 token scales, L2 (and K-split L1) slots
+  static constexpr int ROWBUF = 2 * 1024;
+  static constexpr int OCC = BM <= 64 && 3 * STAGE + ROWBUF <= 80 * 1024 ? 2 : 1;
   // LDS stage buffers: the format's ring depth (or as many as fit) for the
   // large (MFMA-bound) tiles; as many as fit, up to 8, for the small tiles of
   // weight-streaming launches, whose stages are short and need more copies in
   // flight.
-  static constexpr int NBUF_FIT = (160 * 1024 / OCC - (C::NV ? 1024 : 0)) / STAGE;
+  static constexpr int NBUF_FIT = (160 * 1024 / OCC - ROWBUF) / STAGE;
   static constexpr int NBUF = BM >= 128 ? (C::NBUF < NBUF_FIT ? C::NBUF : NBUF_FIT) : (NBUF_FIT < 8 ? NBUF_FIT : 8);
-  static constexpr int ROWS_OFF = NBUF * STAGE;      // per-row epilogue scales (NVFP4)
-  static constexpr int LDS = NBUF * STAGE + (C::NV ? 1024 : 0);
+  static constexpr int ROWS_OFF = NBUF * STAGE;      // the row buffers
+  static constexpr int LDS = NBUF * STAGE + ROWBUF;
+  // A rows one wave copies per stage (contiguous; they wrap modulo BM)
+  static constexpr int A_WROWS = A_STAGE / 4 / C::A_ROW;
   static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // per wave
   static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // per wave
   static constexpr int A_RPI = 1024 / C::A_ROW;         // A rows per copy instruction
@@ -255,7 +260,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   constexpr int SB_N = C::NV ? TN : C::STEPS * TN;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  // the wave index as a wave-uniform (scalar) value
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 5,
+            l32 = lane & 31;
   const int wm = w / G::WN, wn = w % G::WN;
   const int NB = p.N / GEMM_BN;
   // L2 may split K: work unit u covers tile u % tiles and stages
@@ -272,6 +279,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     int e, nb, m0;
     int s0;                 // first K stage of the work unit
     int ks;                 // its K split
+    int par;                // its row buffer
     int64_t a_off[G::A_INSTR];
     const uint8_t* wexp;
     const uint8_t* wsf;
@@ -281,39 +289,48 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     t.ks = uu / tiles;
     t.s0 = t.ks * nstages;
     const int u = uu - t.ks * tiles;
-    // tile -> (expert, n block, m block).  tile_start(e) = (offsets[e] / BM)
-    // * NB is non-decreasing, so the experts with tile_start <= u form a
-    // prefix and u's expert is its last member.  Lanes test 64 experts per
-    // load (four loads in flight), instead of a chain of dependent scalar
-    // loads.
-    int cnt = 0;
-    for (int b = 0; b < p.num_experts; b += 256) {
-      int ts[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = b + 64 * q + lane;
-        ts[q] = i < p.num_experts ? (p.offsets[i] / BM) * NB : 0x7FFFFFFF;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cnt += __builtin_popcountll(ballot(ts[q] <= u));
-    }
-    const int e = cnt - 1;
-    const int mb0 = p.offsets[e] / BM;
-    const int mcount = p.offsets[e + 1] / BM - mb0;
+    // tile -> (expert, n block, m block).  The tiles of expert e are
+    // [mb0 * NB, mb1 * NB) with [mb0, mb1) its BLOCK_M blocks, so u / NB is
+    // one of e's blocks and tile_expert names e.  Scalar loads: the copies in
+    // flight are not waited for.
+    const int e = sload(p.tile_expert + u / NB);
+    const int mb0 = sload(p.offsets + e) / BM;
+    const int mcount = sload(p.offsets + e + 1) / BM - mb0;
     const int local = u - mb0 * NB;
     t.e = e;
     t.nb = local / mcount;
     t.m0 = (mb0 + local % mcount) * BM;
     // per-lane A row offsets for the LDS-DMA copies: lane l of copy i fills
     // LDS row r = A_RPI * (copy index) + l / A_CPR, physical chunk l % A_CPR
-    // (rows wrap modulo BM when a wave has more lanes than rows)
+    // (rows wrap modulo BM when a wave has more lanes than rows).  L1: the
+    // wave's A_WROWS contiguous rows' slots come in by scalar loads and each
+    // lane picks its rows' token.
+    int sv[G::A_WROWS];
+    if constexpr (LAYER != 2) {
+      const int32_t* base = p.sorted_slot + t.m0 + (w * G::A_WROWS) % BM;
+      if constexpr (G::A_WROWS == 8) {
+        const i32x8 v = sload8(base);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = v[j];
+      } else {
+#pragma unroll
+        for (int h = 0; h < G::A_WROWS / 16; ++h) {
+          const i32x16 v = sload16(base + 16 * h);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sv[16 * h + j] = v[j];
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < G::A_INSTR; ++i) {
       const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
       const int r = rl % BM;
       int64_t row;
-      if (LAYER != 2) {
-        const int sl = p.sorted_slot[t.m0 + r];
+      if constexpr (LAYER != 2) {
+        int sl = sv[i * G::A_RPI];
+#pragma unroll
+        for (int k = 1; k < G::A_RPI; ++k)
+          if (lane / G::A_CPR == k) sl = sv[i * G::A_RPI + k];
         row = sl >= 0 ? sl / p.kk : 0;
       } else {
         row = t.m0 + r;
@@ -484,25 +501,38 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     const int base = r * NW;
     return base + NW <= total ? base + xcd * per_xcd + xj : base + (int)blockIdx.x;
   };
+  // Per-row data of tile t into its row buffer, 4 bytes per row, 64 rows per
+  // wave: NVFP4 L1 token scales, L2 (and K-split L1) slots, read by the
+  // tile's epilogue.  Issued a tile ahead, so it is older than that tile's
+  // first copies and the waits before its K loop cover it.
+  constexpr bool ROWDMA = LAYER != 1 || C::NV;
+  auto row_dma = [&](const TileCtx& t) __attribute__((always_inline)) {
+    if constexpr (ROWDMA) {
+      const uint8_t* src = LAYER == 1 ? (const uint8_t*)p.row_scale : (const uint8_t*)p.sorted_slot;
+      if (w * 64 < BM && (BM >= 64 || lane < BM))
+        __builtin_amdgcn_global_load_lds(src + ((int64_t)t.m0 + w * 64 + lane) * 4,
+                                         (lds_void*)(smem + G::ROWS_OFF + t.par * 1024 + w * 256), 4, 0, 0);
+    }
+  };
   const int u0 = unit(0);
   TileCtx ta, tb;
   int cur = 0;           // LDS buffer of the current stage
   bool primed = false;   // the current tile's first NBUF-1 stages are issued
-  if (u0 < total) ta = make_tile(u0);
+  if (u0 < total) {
+    ta = make_tile(u0);
+    ta.par = 0;
+    row_dma(ta);
+  }
   for (int r = 0; unit(r) < total; ++r) {
     const int un = unit(r + 1);
     const bool has_next = un < total;
-    if (has_next) tb = make_tile(un);
+    if (has_next) {
+      tb = make_tile(un);
+      tb.par = ta.par ^ 1;
+    }
     const bool chain_next = chain && has_next;
     lds_barrier();        // every wave is done with the previous tile's LDS
-    // NVFP4 L1: the epilogue's per-row scale, token scale x expert scale
-    // (read after the K loop's barriers)
-    if constexpr (C::NV && LAYER == 1) {   // (a K-split L1 leaves the scales to its finish)
-      if (tid < BM) {
-        const int sl = p.sorted_slot[ta.m0 + tid];
-        ((float*)(smem + G::ROWS_OFF))[tid] = p.a_tok[sl >= 0 ? sl / p.kk : 0] * p.w_gs[ta.e];
-      }
-    }
+    if (has_next) row_dma(tb);
     if (!primed) {
       // a tile the previous one could not prefetch: drain that tile's
       // clamped re-copies, then issue stages 0 .. NBUF-2
@@ -609,6 +639,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // split (LAYER 3): float32 rows per slot (LAYER 3: raw accumulators in
     // the kernel's column order, summed and activated by k_l1_finish).
     if constexpr (LAYER == 1) {
+      const float wgs = C::NV ? __builtin_bit_cast(float, sload(p.w_gs + e)) : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -621,7 +652,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
             float gv = acc[tm][2 * pp][v], uv = acc[tm][2 * pp + 1][v];
             if constexpr (C::NV) {
               // NVFP4 accumulators carry neither the token nor the expert scale
-              const float alpha = ((const float*)(smem + G::ROWS_OFF))[row - m0];
+              const float alpha = ((const float*)(smem + G::ROWS_OFF + ta.par * 1024))[row - m0] * wgs;
               gv *= alpha;
               uv *= alpha;
             }
@@ -632,15 +663,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       }
     } else {
       // NVFP4 L2: w2's expert scale times the L2 input's global scale
-      const float alpha2 = C::NV && LAYER == 2 ? p.w_gs[e] * p.l2_scale : 1.0f;
-      // the slots of the lane's 16 rows per row block, loaded together (four
-      // 16-byte loads each) before any store, so the loads share one wait
+      const float alpha2 = C::NV && LAYER == 2 ? __builtin_bit_cast(float, sload(p.w_gs + e)) * p.l2_scale : 1.0f;
+      // the slots of the lane's 16 rows per row block, from the row buffer
+      const int32_t* rslot = (const int32_t*)(smem + G::ROWS_OFF + ta.par * 1024);
       int slots[TM][16];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int4 s4 = *(const int4*)(p.sorted_slot + m0 + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
+          const int4 s4 = *(const int4*)(rslot + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
           slots[tm][4 * q] = s4.x;
           slots[tm][4 * q + 1] = s4.y;
           slots[tm][4 * q + 2] = s4.z;

@@ -32,6 +32,8 @@ struct GemmArgs {
   // routing
   const int32_t* sorted_slot;
   const int32_t* offsets;  // [E'+1], multiples of BLOCK_M
+  const int32_t* tile_expert;   // [M / BLOCK_M] expert of each BLOCK_M block
+  const float* row_scale;  // NVFP4 L1: token scale of each sorted row (1 if padding)
   const int32_t* meta;     // meta[0] = number of BLOCK_M tiles
   int num_experts;         // E'
   int kk;                  // slots per token (top_k + shared)
@@ -70,9 +72,11 @@ hipError_t gemm_init(int device);
 void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
                     int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream);
 // L1 A-operand block scales x_sf [T, sf_ld] -> block-major planes of the
-// sorted rows: out[kb * plane + m] (rows m < offsets[E]).
+// sorted rows: out[kb * plane + m] (rows m < offsets[E]); with a_tok, also
+// row_scale[m] = a_tok of the row's token (1 for padding).
 void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E, int kk, const uint8_t* x_sf,
-                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, hipStream_t stream);
+                      int sf_ld, int64_t plane, int64_t max_rows, uint8_t fill, uint8_t* out, const float* a_tok,
+                      float* row_scale, hipStream_t stream);
 
 void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream);
 
