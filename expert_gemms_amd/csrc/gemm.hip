@@ -444,7 +444,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // the lane's B-scale dword
 #pragma unroll
       for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
-        NvScale ssa[TM], ssb[TN];
+        f16x2 ssa[TM], ssb[TN];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * h)) & 0xFF);
 #pragma unroll
