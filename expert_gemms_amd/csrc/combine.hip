@@ -14,9 +14,40 @@
 
 namespace moe {
 
-// Workgroup (t, c): token t, columns [1024 c, 1024 c + 1024), 4 per thread;
-// every load of a thread is independent, so a token's k' x nsplit rows stream
-// in together.
+// Weighted sum of token t's slot rows at columns h .. h+3, in slot order.
+// The rows are loaded 8 slots at a time before any is added, so a thread
+// keeps 8 loads in flight; a dropped slot's row (never written) is loaded
+// but not added.
+__device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nsplit, int64_t o_split,
+                                           const int32_t* __restrict__ slot_row,
+                                           const float* __restrict__ topk_w, int t, int k, int kk, int H, int h) {
+  const int64_t s0 = (int64_t)t * kk;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j0 = 0; j0 < kk; j0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (j0 + i < kk) {
+        v[i] = *(const f32x4*)(o + (s0 + j0 + i) * H + h);
+        for (int q = 1; q < nsplit; ++q) v[i] += *(const f32x4*)(o + q * o_split + (s0 + j0 + i) * H + h);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      if (j < kk && slot_row[s0 + j] >= 0) {
+        const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
+        acc[0] += wt * v[i][0];
+        acc[1] += wt * v[i][1];
+        acc[2] += wt * v[i][2];
+        acc[3] += wt * v[i][3];
+      }
+    }
+  }
+  return acc;
+}
+
+// Workgroup (t, c): token t, columns [1024 c, 1024 c + 1024), 4 per thread.
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, int nsplit, int64_t o_split,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ topk_w, int k, int kk, int H,
@@ -24,18 +55,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
   const int t = blockIdx.x;
   const int h = blockIdx.y * 1024 + threadIdx.x * 4;
   if (h >= H) return;
-  const int64_t s0 = (int64_t)t * kk;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < kk; ++j) {
-    if (slot_row[s0 + j] < 0) continue;
-    const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
-    f32x4 v = *(const f32x4*)(o + (s0 + j) * H + h);
-    for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + (s0 + j) * H + h);
-    acc[0] += wt * v[0];
-    acc[1] += wt * v[1];
-    acc[2] += wt * v[2];
-    acc[3] += wt * v[3];
-  }
+  const f32x4 acc = token_sum(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
   uint2 packed;
   packed.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
   packed.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
@@ -53,20 +73,9 @@ __global__ void __launch_bounds__(256) k_combine_norm(const float* __restrict__ 
   extern __shared__ f32x4 rowv[];   // H / 4
   __shared__ float red[4];
   const int t = blockIdx.x;
-  const int64_t s0 = (int64_t)t * kk;
   float ss = 0.0f;
   for (int h = threadIdx.x * 4; h < H; h += 1024) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < kk; ++j) {
-      if (slot_row[s0 + j] < 0) continue;
-      const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
-      f32x4 v = *(const f32x4*)(o + (s0 + j) * H + h);
-      for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + (s0 + j) * H + h);
-      acc[0] += wt * v[0];
-      acc[1] += wt * v[1];
-      acc[2] += wt * v[2];
-      acc[3] += wt * v[3];
-    }
+    const f32x4 acc = token_sum(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
     rowv[h >> 2] = acc;
     ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
   }
