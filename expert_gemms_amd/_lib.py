@@ -67,7 +67,7 @@ def _lib():
         lib.moe_quantize_weights.restype = _I
         lib.moe_quantize_x.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P]
         lib.moe_quantize_x.restype = _I
-        lib.moe_dispatch.argtypes = [_I] * 6 + [_P] * 7
+        lib.moe_dispatch.argtypes = [_I] * 6 + [_P] * 8
         lib.moe_dispatch.restype = _I
         lib.moe_forward.argtypes = ([_I] * 9 + [ctypes.POINTER(Activation), ctypes.POINTER(Options)] + [_P] * 9
                                     + [ctypes.c_float, _P, _P, ctypes.c_size_t, _P])
@@ -136,10 +136,19 @@ def moe_quantize_x(fmt, num_tokens, hidden, x, codes, scales, token_scale=None, 
 
 
 def moe_dispatch(num_tokens, top_k, num_shared, expert_start, num_local_experts, block_m, topk_ids,
-                 counts, offsets, sorted_slot, slot_row, tile_expert, stream=None):
+                 counts, offsets, sorted_slot, slot_row, tile_expert, block_counts=None, stream=None):
+    """``block_counts``: optional int32 scratch of ``dispatch_scratch_ints``
+    values (many-workgroup dispatch from 16384 slots on)."""
     _check(_lib().moe_dispatch(num_tokens, top_k, num_shared, expert_start, num_local_experts, block_m,
                                _ptr(topk_ids), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
-                               _ptr(slot_row), _ptr(tile_expert), _stream(stream)), "moe_dispatch")
+                               _ptr(slot_row), _ptr(tile_expert), _ptr(block_counts), _stream(stream)),
+           "moe_dispatch")
+
+
+def dispatch_scratch_ints(num_tokens, top_k, num_shared, num_local_experts):
+    """Size (int32 values) of moe_dispatch's optional block_counts scratch."""
+    S = num_tokens * (top_k + num_shared)
+    return (S + 2047) // 2048 * (num_local_experts + num_shared)
 
 
 def moe_forward(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,

@@ -69,6 +69,7 @@ struct Workspace {
   int32_t* sorted_slot;
   int32_t* slot_row;
   int32_t* tile_expert;
+  int32_t* block_counts;   // the many-workgroup dispatch's per-chunk counts
   uint8_t* xq;        // dispatch-quantised x codes
   uint8_t* xq_sf;     // its block scales, [T, H / block]
   uint8_t* a1_sf;     // the same in sorted-row planes (one per K block)
@@ -95,6 +96,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   w.sorted_slot = (int32_t*)take(M * 4);
   w.slot_row = (int32_t*)take(S * 4);
   w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
+  w.block_counts = (int32_t*)take(dispatch_scratch_ints(S, (int)E) * 4);
   w.xq = w.xq_sf = w.a1_sf = w.a2 = w.a2_sf = nullptr;
   w.x_tok = w.row_tok = nullptr;
   // a scale plane holds every sorted row plus 256 bytes, so a tile's
@@ -337,7 +339,7 @@ int moe_quantize_x(moe_format_t fmt, int num_tokens, int hidden, const void* x, 
 
 int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start, int num_local_experts, int block_m,
                  const int32_t* topk_ids, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                 int32_t* tile_expert, void* stream) {
+                 int32_t* tile_expert, int32_t* block_counts, void* stream) {
   if (num_tokens < 0 || top_k < 1 || num_shared < 0 || num_local_experts < 1 ||
       num_local_experts + num_shared > MAX_LOCAL_EXPERTS)
     return MOE_E_INVALID;
@@ -349,7 +351,7 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start, in
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, block_m, counts, offsets,
-                  sorted_slot, slot_row, tile_expert, nullptr, (hipStream_t)stream);
+                  sorted_slot, slot_row, tile_expert, nullptr, block_counts, (hipStream_t)stream);
   return hip_status(hipGetLastError());
 }
 
@@ -442,7 +444,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   // a2: routing metadata
   mark(2 * MOE_STEP_DISPATCH);
   launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts, w.offsets,
-                  w.sorted_slot, w.slot_row, w.tile_expert, w.meta, s);
+                  w.sorted_slot, w.slot_row, w.tile_expert, w.meta, w.block_counts, s);
   const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
   const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (scaled) {

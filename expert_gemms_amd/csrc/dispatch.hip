@@ -43,6 +43,44 @@ __device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
   return e >= 0 ? m : 0ull;
 }
 
+// Counting pass over one wave's slots [s0, s1): hist_w[e] += its slots of
+// expert e (the lowest lane of each group of equal experts adds the group).
+__device__ __forceinline__ void wave_count(const int32_t* __restrict__ topk_ids, int s0, int s1, int kk, int k,
+                                           int start, int n_loc, int nbits, int* hist_w, int l) {
+  for (int b = s0; b < s1; b += WAVE) {
+    int s = b + l;
+    int e = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+    uint64_t m = match_mask(e, nbits);
+    if (e >= 0 && (__builtin_ctzll(m) == l)) hist_w[e] += __builtin_popcountll(m);
+  }
+}
+
+// Scatter pass over one wave's slots [s0, s1) in order: slot s of expert e
+// goes to row hist_w[e] + (earlier slots of e in its batch), then the group
+// leader advances hist_w[e]; a dropped slot gets slot_row -1.
+__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ topk_ids, int s0, int s1, int kk, int k,
+                                             int start, int n_loc, int nbits, int* hist_w, int l,
+                                             int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row) {
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  for (int b = s0; b < s1; b += WAVE) {
+    int s = b + l;
+    bool live = s < s1;
+    int e = live ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+    uint64_t m = match_mask(e, nbits);
+    if (e >= 0) {
+      int pos = hist_w[e] + __builtin_popcountll(m & lt_mask);
+      sorted_slot[pos] = s;
+      slot_row[s] = pos;
+    } else if (live) {
+      slot_row[s] = -1;
+    }
+    // every lane has read its base before the group leader bumps it
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && __builtin_ctzll(m) == l) hist_w[e] += __builtin_popcountll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 __global__ void __launch_bounds__(DISPATCH_THREADS)
 k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc,
            int bm, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -52,7 +90,6 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
   __shared__ int wave_tot[DISPATCH_WAVES];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
   const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
-  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
 
   for (int i = tid; i < DISPATCH_WAVES * MAX_LOCAL_EXPERTS; i += DISPATCH_THREADS) (&hist[0][0])[i] = 0;
   __syncthreads();
@@ -62,12 +99,7 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
   const int s0 = min(w * per, S), s1 = min(s0 + per, S);
 
   // pass 1: per-wave histogram
-  for (int b = s0; b < s1; b += WAVE) {
-    int s = b + l;
-    int e = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
-    uint64_t m = match_mask(e, nbits);
-    if (e >= 0 && (__builtin_ctzll(m) == l)) hist[w][e] += __builtin_popcountll(m);
-  }
+  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
   __syncthreads();
 
   // pass 2a: expert tid: exclusive scan of its per-wave counts; padded size
@@ -106,23 +138,7 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
   __syncthreads();
 
   // pass 3: stable scatter
-  for (int b = s0; b < s1; b += WAVE) {
-    int s = b + l;
-    bool live = s < s1;
-    int e = live ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
-    uint64_t m = match_mask(e, nbits);
-    if (e >= 0) {
-      int pos = hist[w][e] + __builtin_popcountll(m & lt_mask);
-      sorted_slot[pos] = s;
-      slot_row[s] = pos;
-    } else if (live) {
-      slot_row[s] = -1;
-    }
-    // every lane has read its base before the group leader bumps it
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0 && __builtin_ctzll(m) == l) hist[w][e] += __builtin_popcountll(m);
-    __builtin_amdgcn_wave_barrier();
-  }
+  wave_scatter(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
 
   // padding rows and the tile -> expert table
   if (tid < E) {
@@ -131,12 +147,126 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
   }
 }
 
+// Many-workgroup dispatch for large slot counts: the same metadata in three
+// launches.  The slots are cut into chunks of DCHUNK (4 waves of 512): a
+// counting launch writes each chunk's per-expert counts to block_counts
+// [chunks, E]; one workgroup scans them per expert (chunk order), lays out
+// the BLOCK_M-padded groups and turns block_counts into each chunk's first
+// row per expert; a scatter launch recounts each chunk per wave and places
+// its slots in order.  Chunks, and waves inside a chunk, are in slot order,
+// so the result equals the single-workgroup kernel's row for row.
+constexpr int DCHUNK = 2048;
+constexpr int DC_WAVES = 4;
+constexpr int DC_PER_WAVE = DCHUNK / DC_WAVES;
+
+__global__ void __launch_bounds__(DC_WAVES * WAVE)
+k_dispatch_count(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc, int nbits,
+                 int32_t* __restrict__ block_counts) {
+  __shared__ int hist[DC_WAVES][MAX_LOCAL_EXPERTS];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
+  for (int i = tid; i < DC_WAVES * MAX_LOCAL_EXPERTS; i += DC_WAVES * WAVE) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int s0 = min(blockIdx.x * DCHUNK + w * DC_PER_WAVE, S), s1 = min(s0 + DC_PER_WAVE, S);
+  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
+  __syncthreads();
+  for (int e = tid; e < E; e += DC_WAVES * WAVE) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < DC_WAVES; ++ww) c += hist[ww][e];
+    block_counts[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, int32_t* __restrict__ counts,
+                int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+                int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+  __shared__ int wave_tot[DISPATCH_WAVES];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  int run = 0;
+  if (tid < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int n = block_counts[(int64_t)c * E + tid];
+      block_counts[(int64_t)c * E + tid] = run;
+      run += n;
+    }
+    counts[tid] = run;
+  }
+  const int v = tid < E ? (run + bm - 1) / bm * bm : 0;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    int o = __shfl_up(incl, d, 64);
+    if (l >= d) incl += o;
+  }
+  if (l == WAVE - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int ww = 0; ww < w; ++ww) wbase += wave_tot[ww];
+  const int off = wbase + incl - v;
+  int total = 0;
+  for (int ww = 0; ww < DISPATCH_WAVES; ++ww) total += wave_tot[ww];
+  if (tid < E) {
+    offsets[tid] = off;
+    for (int c = 0; c < nchunks; ++c) block_counts[(int64_t)c * E + tid] += off;
+    for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
+    for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    if (meta) {
+      meta[0] = total / bm;
+      meta[1] = total;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(DC_WAVES * WAVE)
+k_dispatch_scatter(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc, int nbits,
+                   const int32_t* __restrict__ block_counts, int32_t* __restrict__ sorted_slot,
+                   int32_t* __restrict__ slot_row) {
+  __shared__ int hist[DC_WAVES][MAX_LOCAL_EXPERTS];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
+  for (int i = tid; i < DC_WAVES * MAX_LOCAL_EXPERTS; i += DC_WAVES * WAVE) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int s0 = min(blockIdx.x * DCHUNK + w * DC_PER_WAVE, S), s1 = min(s0 + DC_PER_WAVE, S);
+  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
+  __syncthreads();
+  // each wave's first row per expert: the chunk's base plus the earlier waves
+  for (int e = tid; e < E; e += DC_WAVES * WAVE) {
+    int base = block_counts[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int ww = 0; ww < DC_WAVES; ++ww) {
+      const int c = hist[ww][e];
+      hist[ww][e] = base;
+      base += c;
+    }
+  }
+  __syncthreads();
+  wave_scatter(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
+}
+
+int64_t dispatch_scratch_ints(int64_t S, int E) { return (S + DCHUNK - 1) / DCHUNK * E; }
+
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                     int32_t* tile_expert, int32_t* meta, hipStream_t stream) {
+                     int32_t* tile_expert, int32_t* meta, int32_t* block_counts, hipStream_t stream) {
   int E = n_loc + n_sh;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  const int64_t S = (int64_t)T * (k + n_sh);
+  if (block_counts && S >= DISPATCH_MANY_MIN_SLOTS) {
+    const int nchunks = (int)((S + DCHUNK - 1) / DCHUNK);
+    hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(DC_WAVES * WAVE), 0, stream, topk_ids, T, k, n_sh, start,
+                       n_loc, nbits, block_counts);
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(DISPATCH_THREADS), 0, stream, nchunks, E, bm, block_counts,
+                       counts, offsets, sorted_slot, tile_expert, meta);
+    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(DC_WAVES * WAVE), 0, stream, topk_ids, T, k, n_sh,
+                       start, n_loc, nbits, block_counts, sorted_slot, slot_row);
+    return;
+  }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh, start,
                      n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta);
 }

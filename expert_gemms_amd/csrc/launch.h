@@ -55,9 +55,14 @@ struct GemmArgs {
 
 enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
 
+// Routing metadata; with block_counts (dispatch_scratch_ints(S, E) int32
+// values) and at least DISPATCH_MANY_MIN_SLOTS slots, the many-workgroup
+// kernels (same result), else one workgroup.
+constexpr int64_t DISPATCH_MANY_MIN_SLOTS = 16384;
+int64_t dispatch_scratch_ints(int64_t S, int E);
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                     int32_t* tile_expert, int32_t* meta, hipStream_t stream);
+                     int32_t* tile_expert, int32_t* meta, int32_t* block_counts, hipStream_t stream);
 
 // Sum of the K parts of a split L1 GEMM (a.o, a.ksplit, a.o_split), then its
 // activation and L2-input quantisation into (a.c, a.c_sf).

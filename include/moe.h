@@ -194,13 +194,17 @@ int moe_route(int num_tokens, int num_experts, int top_k, const float* logits, c
  *   slot_row[S]       row of each slot in sorted_slot, -1 if dropped
  *   tile_expert[M/block_m] expert of each block_m-row tile
  * The buffers must hold the maximum sizes (sorted_slot: S + E'(block_m - 1),
- * tile_expert: that / block_m).  This is the kernel moe_forward runs; it is
+ * tile_expert: that / block_m).  This is the dispatch moe_forward runs; it is
  * exported so the metadata can be checked on its own.  topk_ids: int32
- * [T, top_k] (device).  block_m in {32, 64, 128, 256}; E' = num_local_experts + num_shared <= 1000. */
+ * [T, top_k] (device).  block_m in {32, 64, 128, 256}; E' = num_local_experts + num_shared <= 1000.
+ * block_counts: NULL, or device scratch of ceil(S / 2048) * E' int32 values;
+ * with it and S >= 16384 the work is spread over many workgroups (three
+ * launches; moe_forward does this from its workspace), without it one
+ * workgroup does it all.  The metadata are the same either way. */
 int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start,
                  int num_local_experts, int block_m, const int32_t* topk_ids,
                  int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
-                 int32_t* slot_row, int32_t* tile_expert, void* stream);
+                 int32_t* slot_row, int32_t* tile_expert, int32_t* block_counts, void* stream);
 
 /* The layer (DeepGemmMegaMoEExperts.forward on the DeepGEMM MegaMoE page):
  *   out[t] = sum over slots j of w[t, j] * W2_e * act(W13_e * x_t)

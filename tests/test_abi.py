@@ -127,8 +127,8 @@ def test_other_entry_points_validate():
     lib = moe.lib_handle()
     P = ctypes.c_void_p
     f = P(0x10000)
-    assert lib.moe_dispatch(4, 2, 0, 0, 4, 48, f, f, f, f, f, f, None) == _lib.E_INVALID
-    assert lib.moe_dispatch(4, 0, 0, 0, 4, 32, f, f, f, f, f, f, None) == _lib.E_INVALID
+    assert lib.moe_dispatch(4, 2, 0, 0, 4, 48, f, f, f, f, f, f, None, None) == _lib.E_INVALID
+    assert lib.moe_dispatch(4, 0, 0, 0, 4, 32, f, f, f, f, f, f, None, None) == _lib.E_INVALID
     assert lib.moe_quantize_x(0, 4, 256, f, f, f, None, None) == _lib.E_INVALID       # BF16 has no quantiser
     assert lib.moe_quantize_x(1, 4, 100, f, f, f, None, None) == _lib.E_INVALID
     assert lib.moe_quantize_x(3, 4, 256, f, f, f, None, None) == _lib.E_INVALID       # NVFP4 needs token scales

@@ -12,15 +12,18 @@ from synth import CONFIGS, gen_routing
 pytestmark = pytest.mark.gpu
 
 
-def run_dispatch(ids, n_sh, start, n_loc, bm):
+def run_dispatch(ids, n_sh, start, n_loc, bm, many=False):
+    """many: pass the block_counts scratch (the many-workgroup kernels run
+    from 16384 slots on)."""
     T, k = ids.shape
     E = n_loc + n_sh
     S = T * (k + n_sh)
     M = S + E * (bm - 1)
     d = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
     counts, offsets, ss, sr, te = d(E), d(E + 1), d(M), d(S), d(M // bm + 1)
+    bc = d(moe._lib.dispatch_scratch_ints(T, k, n_sh, n_loc)) if many else None
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
-    moe.moe_dispatch(T, k, n_sh, start, n_loc, bm, ids_d, counts, offsets, ss, sr, te)
+    moe.moe_dispatch(T, k, n_sh, start, n_loc, bm, ids_d, counts, offsets, ss, sr, te, block_counts=bc)
     torch.cuda.synchronize()
     c = lambda t: t.cpu().numpy()
     off = c(offsets)
@@ -70,3 +73,31 @@ def test_dispatch_skewed_and_single_expert():
     ref = dispatch_reference(ids1, 0, 0, 8, 128)
     for key in ref:
         assert np.array_equal(got[key], ref[key]), key
+
+
+# Slot counts from 16384 on, where moe_forward's dispatch runs on many
+# workgroups: bit-exact against the oracle and against the one-workgroup
+# kernel (partial last chunks, dropped slots, a shared expert, many experts).
+MANY_CASES = [
+    # (T, k, E_ids, n_sh, start, n_loc, bm)
+    (8192, 8, 256, 1, 0, 256, 128),
+    (16384, 6, 64, 0, 0, 64, 128),
+    (3001, 6, 600, 0, 0, 600, 32),
+    (2100, 8, 16, 0, 4, 8, 64),
+    (2048, 8, 8, 0, 0, 8, 256),
+]
+
+
+@pytest.mark.parametrize("case", MANY_CASES)
+def test_dispatch_many_workgroups_bit_exact(case):
+    T, k, Eids, n_sh, start, n_loc, bm = case
+    assert T * (k + n_sh) >= 16384
+    rng = np.random.default_rng(sum(case))
+    ids = rng.integers(-1, Eids, (T, k)).astype(np.int32)
+    ids[rng.random((T, k)) < 0.02] = 9999
+    many = run_dispatch(ids, n_sh, start, n_loc, bm, many=True)
+    one = run_dispatch(ids, n_sh, start, n_loc, bm)
+    ref = dispatch_reference(ids, n_sh, start, n_loc, bm)
+    for key in ref:
+        assert np.array_equal(many[key], ref[key]), key
+        assert np.array_equal(many[key], one[key]), key

@@ -102,7 +102,10 @@ def test_fullsize_sampled(name, tokens):
     d = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
     cnt, off, ss, sr, te = d(E_all), d(E_all + 1), d(M), d(S), d(M // bm + 1)
     ids_d = dev(ids)
-    moe.moe_dispatch(T, cfg.top_k, cfg.num_shared, 0, cfg.E, bm, ids_d, cnt, off, ss, sr, te)
+    # with the scratch moe_forward's workspace provides (many workgroups from
+    # 16384 slots on, as in the forward)
+    bc = d(moe._lib.dispatch_scratch_ints(T, cfg.top_k, cfg.num_shared, cfg.E))
+    moe.moe_dispatch(T, cfg.top_k, cfg.num_shared, 0, cfg.E, bm, ids_d, cnt, off, ss, sr, te, block_counts=bc)
     ref_d = dispatch_reference(ids, cfg.num_shared, 0, cfg.E, bm)
     Mp = int(ref_d["offsets"][-1])
     got = {"counts": cnt.cpu().numpy()[:E_all], "offsets": off.cpu().numpy(), "sorted_slot": ss.cpu().numpy()[:Mp],
