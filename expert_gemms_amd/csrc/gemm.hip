@@ -351,13 +351,16 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       g2lds16(p.a + t.a_off[c] + (int64_t)(t.s0 + s) * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
     } else if constexpr (c < SC) {
       // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
-      // global [layout stage][32-row block][KS_PER_L K-steps][FRAG]
+      // global BF16 [N block][layout stage][32-row block of 8][KS_PER_L
+      // K-steps][FRAG], others [layout stage][32-row block][KS_PER_L][FRAG]
       const int q = w * G::B_INSTR + (c - G::A_INSTR);
       const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
       const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
       const int kg = (t.s0 + s) * C::STEPS + ksl;
-      const uint8_t* src = t.wexp + ((int64_t)(kg / C::KS_PER_L) * (p.N / 32) + t.nb * 8 + nf) * (C::KS_PER_L * C::FRAG) +
-                           (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
+      constexpr int LSK = C::KSTAGE / C::STEPS * C::KS_PER_L;   // K per layout stage
+      const int64_t blk = FMT == F_BF16 ? ((int64_t)t.nb * (p.K / LSK) + kg / C::KS_PER_L) * 8 + nf
+                                        : (int64_t)(kg / C::KS_PER_L) * (p.N / 32) + t.nb * 8 + nf;
+      const uint8_t* src = t.wexp + blk * (C::KS_PER_L * C::FRAG) + (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
       g2lds16(src, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
       // A scales: K block w % (blocks per stage) of this stage, the plane's

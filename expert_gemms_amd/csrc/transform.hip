@@ -15,10 +15,12 @@
 //                     in bytes 16-31 of lane group g)
 //   FP4  (32x32x64):  1 KiB, lane l = row l%32, bytes [32ks + 16(l/32), +16)
 //                     (4-bit operands hold K [32g, 32g+32) contiguously)
-// Fragments are ordered [K stage][32-row block][K-step within the stage]
-// (a stage is 64 K for BF16, 128 K otherwise), so the 8 blocks one tile reads
-// in a stage, and the blocks of neighbouring tiles, are contiguous rather than
-// a large power-of-two stride apart on the same memory channel.  UE8M0 scales
+// BF16 fragments are ordered [256-row N block][64-K stage][32-row block of
+// the 8][K-step within the stage], so the weights one 256-column tile streams
+// over all of K are one contiguous run (measured 2.5 % faster for the
+// MFMA-bound BF16 GEMMs).  The other formats keep [128-K stage][32-row block]
+// [K-step within the stage]: the blocks of the tiles that run side by side
+// are adjacent (measured faster for weight-streaming launches).  UE8M0 scales
 // become [128-K stage][32-row block][lane][2]: byte j of lane l is the scale
 // of row l%32, block 4*stage + 2j + l/32, the byte the scaled MFMA of K-step
 // j takes from that lane.
@@ -37,28 +39,41 @@ __global__ void __launch_bounds__(256) k_transform_codes(const uint8_t* __restri
   const int64_t e = c / chunks_per_expert, ce = c % chunks_per_expert;
   int n, kbyte;
   int64_t row_bytes;
-  const int nfs = N / 32;
+  const int nls = FMT == F_BF16 ? K / 64 : K / 128;   // K stages
+  // BF16: rest = (N block * nls + stage) * 8 + block within the N block;
+  // others: rest = stage * (N / 32) + block
+  auto split = [&](int64_t rest, int& nf, int& stage) {
+    if (FMT == F_BF16) {
+      const int64_t t2 = rest >> 3;
+      nf = (int)((t2 / nls) * 8 + (rest & 7));
+      stage = (int)(t2 % nls);
+    } else {
+      nf = (int)(rest % (N / 32));
+      stage = (int)(rest / (N / 32));
+    }
+  };
+  int nf, stage;
   if (FMT == F_BF16) {
-    const int64_t f = ce >> 6;                  // [stage][nf][4 K-steps of 16]
+    const int64_t f = ce >> 6;                  // [.. block][4 K-steps of 16]
     const int l = (int)(ce & 63);
-    const int64_t rest = f >> 2;
-    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 4 + (int)(f & 3);
+    split(f >> 2, nf, stage);
+    const int ks = stage * 4 + (int)(f & 3);
     n = nf * 32 + (l & 31);
     kbyte = ks * 32 + (l >> 5) * 16;
     row_bytes = (int64_t)K * 2;
   } else if (FMT == F_MXFP8) {
-    const int64_t f = ce >> 7;                  // [stage][nf][2 K-steps of 64]
+    const int64_t f = ce >> 7;                  // [.. block][2 K-steps of 64]
     const int within = (int)(ce & 127), j = within >> 6, l = within & 63;
-    const int64_t rest = f >> 1;
-    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 2 + (int)(f & 1);
+    split(f >> 1, nf, stage);
+    const int ks = stage * 2 + (int)(f & 1);
     n = nf * 32 + (l & 31);
     kbyte = ks * 64 + 32 * j + 16 * (l >> 5);
     row_bytes = K;
   } else {  // FP4
-    const int64_t f = ce >> 6;                  // [stage][nf][2 K-steps of 64]
+    const int64_t f = ce >> 6;                  // [.. block][2 K-steps of 64]
     const int l = (int)(ce & 63);
-    const int64_t rest = f >> 1;
-    const int nf = (int)(rest % nfs), ks = (int)(rest / nfs) * 2 + (int)(f & 1);
+    split(f >> 1, nf, stage);
+    const int ks = stage * 2 + (int)(f & 1);
     n = nf * 32 + (l & 31);
     kbyte = ks * 32 + 16 * (l >> 5);
     row_bytes = K / 2;
