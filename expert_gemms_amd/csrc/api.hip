@@ -484,7 +484,6 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g.tile_expert = w.tile_expert;
   g.row_scale = w.row_tok;
   g.meta = w.meta;
-  g.num_experts = E;
   g.kk = (int)kk;
   g.c = w.a2;
   g.c_sf = w.a2_sf;

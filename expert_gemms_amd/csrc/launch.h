@@ -35,7 +35,6 @@ struct GemmArgs {
   const int32_t* tile_expert;   // [M / BLOCK_M] expert of each BLOCK_M block
   const float* row_scale;  // NVFP4 L1: token scale of each sorted row (1 if padding)
   const int32_t* meta;     // meta[0] = number of BLOCK_M tiles
-  int num_experts;         // E'
   int kk;                  // slots per token (top_k + shared)
   // L1 epilogue: activation + L2-input quantisation into (c, c_sf)
   uint8_t* c;
