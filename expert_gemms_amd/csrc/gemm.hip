@@ -258,6 +258,13 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   // per row / column block and K-step
   constexpr int SA_N = C::NV ? 2 * TM : C::STEPS * TM;
   constexpr int SB_N = C::NV ? TN : C::STEPS * TN;
+  // L1 passes the weights as the MFMA's first operand: accumulator element v
+  // of lane l is then intermediate column 8 (v / 4) + 4 (l / 32) + v % 4 of
+  // its 32-column block for sorted row l % 32, so a row's 32 columns sit in
+  // two lanes and the L2-input quantiser's block maxima need one cross-lane
+  // step per 16 values.  L2 and the K-split L1 keep the rows on the first
+  // operand (a lane's 16 values lie in one column, stored as runs of a row).
+  constexpr bool WFIRST = LAYER == 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   // the wave index as a wave-uniform (scalar) value
@@ -464,7 +471,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
-              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[tm], b8[tn], acc[tm][tn], 0, 0, 0);
+              acc[tm][tn] = WFIRST ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b8[tn], a8[tm], acc[tm][tn], 0, 0, 0)
+                                   : __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[tm], b8[tn], acc[tm][tn], 0, 0, 0);
         }
       }
     } else {
@@ -472,8 +480,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          if constexpr (FMT == F_BF16) {
+          if constexpr (FMT == F_BF16 && WFIRST) {
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tm][tn], 0, 0, 0);
+          } else if constexpr (FMT == F_BF16) {
             acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+          } else if constexpr (WFIRST) {
+            // operand formats: weights FP4 (MXFP4) or FP8, activations FP8
+            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf[tn], af[tm], acc[tm][tn], FMT == F_MXFP4 ? 4 : 0, 0, 0, (int)sb[ks * TN + tn], 0,
+                (int)sa[ks * TM + tm]);
           } else {
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[ks * TM + tm], 0,
@@ -645,22 +660,23 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const float wgs = C::NV ? __builtin_bit_cast(float, sload(p.w_gs + e)) : 1.0f;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
+        const int row = m0 + wm * TM * 32 + tm * 32 + l32;   // the lane's sorted row
+        // NVFP4 accumulators carry neither the token nor the expert scale
+        const float alpha = C::NV ? ((const float*)(smem + G::ROWS_OFF + ta.par * 1024))[row - m0] * wgs : 1.0f;
 #pragma unroll
         for (int pp = 0; pp < TN / 2; ++pp) {
-          const int icol = nb * (GEMM_BN / 2) + (wn * (TN / 2) + pp) * 32 + l32;
-          const int row0 = m0 + wm * TM * 32 + tm * 32 + 4 * g;
+          const int icol0 = nb * (GEMM_BN / 2) + (wn * (TN / 2) + pp) * 32;
+          float a[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = row0 + 8 * (v >> 2) + (v & 3);
             float gv = acc[tm][2 * pp][v], uv = acc[tm][2 * pp + 1][v];
             if constexpr (C::NV) {
-              // NVFP4 accumulators carry neither the token nor the expert scale
-              const float alpha = ((const float*)(smem + G::ROWS_OFF + ta.par * 1024))[row - m0] * wgs;
               gv *= alpha;
               uv *= alpha;
             }
-            store_l2_input<FMT>(act_swiglu(gv, uv, p), row, icol, l32, p);
+            a[v] = act_swiglu(gv, uv, p);
           }
+          store_l2_input_rows<FMT>(a, row, icol0, g, p);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

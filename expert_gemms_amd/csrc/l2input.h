@@ -60,4 +60,64 @@ __device__ __forceinline__ void store_l2_input(float a, int64_t row, int icol, i
   }
 }
 
+// The same quantisation for the L1 epilogue's layout: the lane holds
+// activations a[4j + i] of sorted row `row`, intermediate columns
+// icol0 + 8j + 4g + i (g = lane / 32), and lane l ^ 32 holds the rest of the
+// 32 columns from icol0 on.  Block maxima: the lane's values, then the
+// partner's; codes and scales are those store_l2_input writes for the same
+// activations.  Stores: 4 consecutive columns at a time.
+template <int FMT>
+__device__ __forceinline__ void store_l2_input_rows(const float (&a)[16], int64_t row, int icol0, int g,
+                                                    const GemmArgs& p) {
+  if constexpr (FMT == F_NVFP4) {
+#pragma clang fp contract(off)
+    const float six_g = 6.0f * p.l2_scale;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // 16-column block h: values 8h .. 8h+7
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(a[8 * h + i]));
+      amax = __builtin_fmaxf(amax, shfl_xor(amax, 32));
+      const uint32_t bs = e4m3_encode(amax / six_g);
+      const float bsv = e4m3_decode(bs);
+      const float r = bsv != 0.0f ? 1.0f / (bsv * p.l2_scale) : 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * h + jj;
+        uint32_t q = 0;
+        if (bsv != 0.0f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q |= e2m1_encode(a[4 * j + i] * r) << (4 * i);
+        }
+        *(uint16_t*)(p.c + row * p.c_ld + ((icol0 + 8 * j + 4 * g) >> 1)) = (uint16_t)q;
+      }
+      if (g == h) p.c_sf[(int64_t)((icol0 >> 4) + h) * p.c_sf_ld + row] = (uint8_t)bs;
+    }
+  } else if constexpr (FMT == F_BF16) {
+    uint16_t* out = (uint16_t*)(p.c + row * p.c_ld) + icol0 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(uint2*)(out + 8 * j) = make_uint2((uint32_t)bf16_rne(a[4 * j]) | ((uint32_t)bf16_rne(a[4 * j + 1]) << 16),
+                                          (uint32_t)bf16_rne(a[4 * j + 2]) | ((uint32_t)bf16_rne(a[4 * j + 3]) << 16));
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(a[v]));
+    amax = __builtin_fmaxf(amax, shfl_xor(amax, 32));
+    int c = 0;
+    if (amax > 0.0f) c = mx_scale_code<false>(amax);
+    uint8_t* out = p.c + row * p.c_ld + icol0 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t q = 0;
+      if (amax > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q |= e4m3_encode(__builtin_ldexpf(a[4 * j + i], 127 - c)) << (8 * i);
+      }
+      *(uint32_t*)(out + 8 * j) = q;
+    }
+    if (g == 0) p.c_sf[(int64_t)(icol0 >> 5) * p.c_sf_ld + row] = (uint8_t)c;
+  }
+}
+
 }  // namespace moe
