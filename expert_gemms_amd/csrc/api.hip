@@ -147,13 +147,19 @@ double expected_padded(double m, int bm) {
 
 // BLOCK_M from the expected group sizes (routed experts T*k/n_loc rows,
 // shared experts T): each candidate's expected padded row count is weighed by
-// the tile's relative MFMA efficiency (smaller tiles re-read more operand
-// bytes per FLOP); the cheapest wins.  The block-scaled formats stop at 128
-// (their 256-row tiles run out of registers).
+// the tile's relative efficiency (smaller tiles re-read more operand bytes
+// per FLOP); the cheapest wins.  The block-scaled formats stop at 128 (their
+// 256-row tiles run out of registers).  NVFP4 is measured apart: its GEMMs
+// convert every E2M1 fragment to FP16 in registers, and 64-row tiles, which
+// run two workgroups per CU, overlap one workgroup's conversions with the
+// other's MFMAs (64 rows: 1.13 ms for both GEMMs of the 16384-token layer,
+// 128 rows: 1.24 ms, 32 rows: 1.53 ms).
 int block_m_rule(int T, int n_loc, int n_sh, int k, int fmt) {
   const double routed = (double)T * k / n_loc;
   const int cand[4] = {32, 64, 128, 256};
-  const double eff[4] = {0.35, 0.55, 0.85, 1.0};
+  const double eff_mfma[4] = {0.35, 0.55, 0.85, 1.0};
+  const double eff_nv[4] = {0.70, 1.0, 0.90, 0.0};
+  const double* eff = fmt == MOE_FMT_NVFP4 ? eff_nv : eff_mfma;
   const int nc = fmt == MOE_FMT_BF16 ? 4 : 3;
   int best = 32;
   double best_cost = -1.0;
@@ -520,6 +526,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   g2.K = (int)I;
   g2.o = w.o;
   g2.ksplit = ks;
+  g2.o_bf16 = scaled && ks == 1;
   g2.o_split = (int64_t)T * kk * H;
   mark(2 * MOE_STEP_L2);
   e = launch_gemm(fmt, 2, bm, g2, grid, s);
@@ -528,7 +535,7 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
 
   // a7: weighted combine
   mark(2 * MOE_STEP_COMBINE);
-  launch_combine(w.o, ks, (int64_t)T * kk * H, w.slot_row, o.apply_router_weight_on_input ? nullptr : topk_weights,
+  launch_combine(w.o, g2.o_bf16, ks, (int64_t)T * kk * H, w.slot_row, o.apply_router_weight_on_input ? nullptr : topk_weights,
                  num_tokens, top_k, (int)kk, (int)H, o.post_expert_norm_gamma, o.post_expert_norm_eps,
                  (uint16_t*)out, s);
   mark(2 * MOE_STEP_COMBINE + 1);

@@ -1,6 +1,8 @@
 // Top-k combine: y[t] = sum_j w[t, j] * O[t * k' + j], one round to BF16.
 // When the L2 GEMM split K, O[slot] is the sum of its parts, added in part
-// order before the weighting.
+// order before the weighting.  The rows are float32 for BF16 layers and split
+// L2s, BF16 for the block-scaled formats (the L2 output in the activation
+// dtype, as the unfused decomposition keeps it); the sum is float32 either way.
 //
 // The weighted un-permute-and-reduce of the "fused_moe" page's
 // DeepGemmExperts.apply (deepgemm_unpermute_and_reduce; CutlassExpertsFp8
@@ -14,10 +16,26 @@
 
 namespace moe {
 
+// Columns h .. h+3 of slot row s: float32 rows (with K split, the parts
+// added in part order) or BF16 rows (one part).
+template <bool O16>
+__device__ __forceinline__ f32x4 slot_cols(const float* __restrict__ o, int nsplit, int64_t o_split, int64_t s,
+                                           int H, int h) {
+  if constexpr (O16) {
+    const uint2 b = *(const uint2*)((const uint16_t*)o + s * H + h);
+    return (f32x4){u2f(b.x << 16), u2f(b.x & 0xFFFF0000u), u2f(b.y << 16), u2f(b.y & 0xFFFF0000u)};
+  } else {
+    f32x4 v = *(const f32x4*)(o + s * H + h);
+    for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + s * H + h);
+    return v;
+  }
+}
+
 // Weighted sum of token t's slot rows at columns h .. h+3, in slot order.
 // The rows are loaded 8 slots at a time before any is added, so a thread
 // keeps 8 loads in flight; a dropped slot's row (never written) is loaded
 // but not added.
+template <bool O16>
 __device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nsplit, int64_t o_split,
                                            const int32_t* __restrict__ slot_row,
                                            const float* __restrict__ topk_w, int t, int k, int kk, int H, int h) {
@@ -27,10 +45,7 @@ __device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nspl
     f32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (j0 + i < kk) {
-        v[i] = *(const f32x4*)(o + (s0 + j0 + i) * H + h);
-        for (int q = 1; q < nsplit; ++q) v[i] += *(const f32x4*)(o + q * o_split + (s0 + j0 + i) * H + h);
-      }
+      if (j0 + i < kk) v[i] = slot_cols<O16>(o, nsplit, o_split, s0 + j0 + i, H, h);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -48,6 +63,7 @@ __device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nspl
 }
 
 // Workgroup (t, c): token t, columns [1024 c, 1024 c + 1024), 4 per thread.
+template <bool O16>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, int nsplit, int64_t o_split,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ topk_w, int k, int kk, int H,
@@ -55,7 +71,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
   const int t = blockIdx.x;
   const int h = blockIdx.y * 1024 + threadIdx.x * 4;
   if (h >= H) return;
-  const f32x4 acc = token_sum(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
+  const f32x4 acc = token_sum<O16>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
   uint2 packed;
   packed.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
   packed.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
@@ -65,6 +81,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
 // With the post-expert RMSNorm: one workgroup per token keeps the float32 row
 // in LDS, sums its squares, then writes y / sqrt(mean(y^2) + eps) * gamma.
 // The weighting matches k_combine element for element.
+template <bool O16>
 __global__ void __launch_bounds__(256) k_combine_norm(const float* __restrict__ o, int nsplit, int64_t o_split,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ topk_w, int k, int kk, int H,
@@ -75,7 +92,7 @@ __global__ void __launch_bounds__(256) k_combine_norm(const float* __restrict__ 
   const int t = blockIdx.x;
   float ss = 0.0f;
   for (int h = threadIdx.x * 4; h < H; h += 1024) {
-    const f32x4 acc = token_sum(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
+    const f32x4 acc = token_sum<O16>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
     rowv[h >> 2] = acc;
     ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
   }
@@ -111,14 +128,22 @@ __global__ void __launch_bounds__(256) k_scale_rows(const uint16_t* __restrict__
   }
 }
 
-void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
-                    int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
-  if (gamma)
-    hipLaunchKernelGGL(k_combine_norm, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split, slot_row,
+void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, const int32_t* slot_row,
+                    const float* topk_w, int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out,
+                    hipStream_t stream) {
+  const dim3 grid(T, (H + 1023) / 1024);
+  if (gamma && o_bf16)
+    hipLaunchKernelGGL(k_combine_norm<true>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split, slot_row,
                        topk_w, k, kk, H, gamma, eps, out);
+  else if (gamma)
+    hipLaunchKernelGGL(k_combine_norm<false>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
+                       slot_row, topk_w, k, kk, H, gamma, eps, out);
+  else if (o_bf16)
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
+                       out);
   else
-    hipLaunchKernelGGL(k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, stream, o, nsplit, o_split, slot_row,
-                       topk_w, k, kk, H, out);
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
+                       out);
 }
 
 void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream) {

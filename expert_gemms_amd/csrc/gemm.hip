@@ -697,15 +697,25 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           slots[tm][4 * q + 3] = s4.w;
         }
       }
+      // block-scaled L2 with K unsplit: BF16 rows (the output dtype the
+      // combine reads); else float32 rows (BF16 layers, K parts, split L1)
+      const bool o16 = FMT != F_BF16 && LAYER == 2 && p.o_bf16;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int slot = slots[tm][v];
           if (slot < 0) continue;
-          float* orow = p.o + ta.ks * p.o_split + (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
+          const int64_t col = (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
+          if (o16) {
+            uint16_t* orow = (uint16_t*)p.o + col;
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
+            for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]);
+          } else {
+            float* orow = p.o + ta.ks * p.o_split + col;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
+          }
         }
       }
     }

@@ -50,6 +50,9 @@ struct GemmArgs {
   float* o;
   int ksplit;
   int64_t o_split;
+  // L2 of a block-scaled layer with K unsplit: the rows of o are BF16 (RNE of
+  // the float32 accumulators), [S, N] uint16
+  int o_bf16;
 };
 
 enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
@@ -73,7 +76,7 @@ hipError_t gemm_init(int device);
 
 // Combine (topk_w NULL: every slot weighs 1); gamma non-NULL adds the
 // post-expert RMSNorm.
-void launch_combine(const float* o, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
+void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
                     int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream);
 // L1 A-operand block scales x_sf [T, sf_ld] -> block-major planes of the
 // sorted rows: out[kb * plane + m] (rows m < offsets[E]); with a_tok, also

@@ -41,11 +41,12 @@ def test_block_m_rule():
     assert moe.moe_get_block_m(4096, 8, 0, 2, "bf16") == 256      # 1024 rows per expert
     assert moe.moe_get_block_m(1, 128, 0, 8, "mxfp4") == 32
     assert moe.moe_get_block_m(256, 128, 0, 8, "mxfp4") == 32      # 16 rows per expert
-    assert moe.moe_get_block_m(1000, 64, 0, 6, "nvfp4") == 128     # 93.75
+    assert moe.moe_get_block_m(1000, 64, 0, 6, "nvfp4") == 64      # 93.75; NVFP4 prefers 64-row tiles
     assert moe.moe_get_block_m(0, 8, 0, 2, "bf16") == 32
     # 256 expected rows per routed expert: half the groups spill past 256
     assert moe.moe_get_block_m(8192, 256, 1, 8, "mxfp8") == 128
-    assert moe.moe_get_block_m(16384, 64, 0, 6, "nvfp4") == 128     # block-scaled formats stop at 128
+    assert moe.moe_get_block_m(16384, 64, 0, 6, "nvfp4") == 64
+    assert moe.moe_get_block_m(16384, 64, 0, 6, "mxfp4") == 128     # block-scaled formats stop at 128
     assert moe.moe_get_block_m(16384, 64, 0, 6, "mxfp8") == 128
     assert moe.moe_get_block_m(16384, 64, 0, 6, "bf16") == 256
     with pytest.raises(moe.MoEError):
