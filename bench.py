@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="mixtral_bf16")
     p.add_argument("--tokens", type=int, default=None, help="token count (decode workload)")
-    p.add_argument("--flush-mb", type=int, default=0, help="write this many MB between steps (defeats the MALL)")
+    p.add_argument("--flush-mb", type=int, default=0,
+                   help="read this many MB between steps (evicts the weights from the 256 MB MALL without "
+                        "leaving dirty lines to write back during the step)")
     p.add_argument("--block-m", type=int, default=0, help="BLOCK_M (0: the library's rule)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
@@ -297,7 +299,11 @@ def main():
     layer, x, ids, wts, ids_d, wts_d, canon = build_layer(cfg, T, device)
     out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=device)
     stream = torch.cuda.current_stream()
-    flush = torch.empty(args.flush_mb * (1 << 20), dtype=torch.uint8, device=device) if args.flush_mb else None
+    flush = torch.ones(args.flush_mb * (1 << 18), dtype=torch.int32, device=device) if args.flush_mb else None
+    flush_sink = torch.zeros((), dtype=torch.int64, device=device)
+
+    def evict():
+        flush_sink.add_(flush.sum())
 
     nsteps = len(moe._lib.STEPS)
 
@@ -327,7 +333,7 @@ def main():
     else:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for i in range(args.steps):
-            flush.fill_(i & 0xFF)
+            evict()
             evs[i][0].record(stream)
             fwd()
             evs[i][1].record(stream)
@@ -341,11 +347,14 @@ def main():
     torch.cuda.synchronize()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            evict()
         layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m, step_events=step_events[i])
     torch.cuda.synchronize()
     per_step = {name: float(np.mean([ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in step_events]))
                 for j, name in enumerate(moe._lib.STEPS)}
+    # spread of the whole step over those K steps (first step event to last)
+    totals = [ev[0].elapsed_time(ev[2 * len(moe._lib.STEPS) - 1]) for ev in step_events]
+    step_pct = {q: round(float(np.percentile(totals, q)), 4) for q in (10, 50, 90)}
 
     # secondary: the step captured once in a HIP graph and replayed (launch
     # overhead removed); the replay's output is checked against the eager one
@@ -416,6 +425,7 @@ def main():
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "mfma_frac": round(tflops / peak, 4),
         "step_ms": {k: round(v, 4) for k, v in per_step.items()},
+        "step_ms_p10_p50_p90": [step_pct[10], step_pct[50], step_pct[90]],
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "wall_s": round(wall, 3),
         "roofline": roof,
