@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", default="mixtral_bf16")
     p.add_argument("--tokens", type=int, default=None, help="token count (decode workload)")
     p.add_argument("--flush-mb", type=int, default=0,
