@@ -62,6 +62,50 @@ __device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nspl
   return acc;
 }
 
+// The same sum over BF16 slot rows at columns h .. h+7: one 16-byte load per
+// row, the additions of each column in the same order and form as token_sum.
+__device__ __forceinline__ void token_sum8(const uint16_t* __restrict__ o16, const int32_t* __restrict__ slot_row,
+                                           const float* __restrict__ topk_w, int t, int k, int kk, int H, int h,
+                                           float (&acc)[8]) {
+  const int64_t s0 = (int64_t)t * kk;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  for (int j0 = 0; j0 < kk; j0 += 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (j0 + i < kk) v[i] = *(const uint4*)(o16 + (s0 + j0 + i) * H + h);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + i;
+      if (j < kk && slot_row[s0 + j] >= 0) {
+        const float wt = j < k && topk_w ? topk_w[(int64_t)t * k + j] : 1.0f;
+        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += wt * u2f((c & 1) ? (wd[c >> 1] & 0xFFFF0000u) : (wd[c >> 1] << 16));
+      }
+    }
+  }
+}
+
+// BF16 slot rows: workgroup (t, c) takes token t, columns [2048 c, 2048 c +
+// 2048), 8 per thread.
+__global__ void __launch_bounds__(256) k_combine16(const uint16_t* __restrict__ o16,
+                                                   const int32_t* __restrict__ slot_row,
+                                                   const float* __restrict__ topk_w, int k, int kk, int H,
+                                                   uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * 2048 + threadIdx.x * 8;
+  if (h >= H) return;
+  float acc[8];
+  token_sum8(o16, slot_row, topk_w, t, k, kk, H, h, acc);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bf16_rne(acc[2 * i]) | ((uint32_t)bf16_rne(acc[2 * i + 1]) << 16);
+  *(uint4*)(out + (int64_t)t * H + h) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Workgroup (t, c): token t, columns [1024 c, 1024 c + 1024), 4 per thread.
 template <bool O16>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, int nsplit, int64_t o_split,
@@ -139,8 +183,8 @@ void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, con
     hipLaunchKernelGGL(k_combine_norm<false>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
                        slot_row, topk_w, k, kk, H, gamma, eps, out);
   else if (o_bf16)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
-                       out);
+    hipLaunchKernelGGL(k_combine16, dim3(T, (H + 2047) / 2048), dim3(256), 0, stream, (const uint16_t*)o, slot_row,
+                       topk_w, k, kk, H, out);
   else
     hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
                        out);
