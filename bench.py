@@ -352,8 +352,19 @@ def main():
     torch.cuda.synchronize()
     per_step = {name: float(np.mean([ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in step_events]))
                 for j, name in enumerate(moe._lib.STEPS)}
-    # spread of the whole step over those K steps (first step event to last)
-    totals = [ev[0].elapsed_time(ev[2 * len(moe._lib.STEPS) - 1]) for ev in step_events]
+    # spread of the step time: K more steps, each between one pair of events
+    # (no events inside the step; each pair adds a few microseconds, which
+    # shows at decode sizes)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            evict()
+        pairs[i][0].record(stream)
+        fwd()
+        pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    totals = [a.elapsed_time(b) for a, b in pairs]
     step_pct = {q: round(float(np.percentile(totals, q)), 4) for q in (10, 50, 90)}
 
     # secondary: the step captured once in a HIP graph and replayed (launch
