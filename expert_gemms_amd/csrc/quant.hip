@@ -10,6 +10,7 @@
 // scale bs = E4M3(amax16 / (6 g)), elements E2M1(v * (1 / (bs g))), all in
 // float32 arithmetic.  The token scale is amax_t / (6 * 448).
 #include "common.h"
+#include "l2input.h"
 #include "launch.h"
 
 namespace moe {
@@ -22,7 +23,9 @@ __device__ __forceinline__ float load_elem(const void* src, int64_t i) {
 }
 
 // One thread per 32-element MX block.  Element codes are written unpacked
-// for E4M3 and two per byte for E2M1.
+// for E4M3 and two per byte for E2M1, by the hardware converts (equal to the
+// software encoders here: the scaled block maximum is at most the format's
+// largest value).
 template <bool F32, bool FP4>
 __global__ void __launch_bounds__(256) k_quant_mx(const void* __restrict__ src, int64_t nblocks,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -37,33 +40,25 @@ __global__ void __launch_bounds__(256) k_quant_mx(const void* __restrict__ src, 
     amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
   }
   int c = 0;
-  uint32_t q[32];
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (amax > 0.0f) {
     c = mx_scale_code<FP4>(amax);
+    float x[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float x = __builtin_ldexpf(v[i], 127 - c);
-      q[i] = FP4 ? e2m1_encode(x) : e4m3_encode(x);
+    for (int i = 0; i < 32; ++i) x[i] = __builtin_ldexpf(v[i], 127 - c);
+#pragma unroll
+    for (int j = 0; j < (FP4 ? 4 : 8); ++j) {
+      if constexpr (FP4)
+        w[j] = e2m1_x4(x[8 * j], x[8 * j + 1], x[8 * j + 2], x[8 * j + 3]) |
+               (e2m1_x4(x[8 * j + 4], x[8 * j + 5], x[8 * j + 6], x[8 * j + 7]) << 16);
+      else
+        w[j] = e4m3_x4_mx(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) q[i] = 0;
   }
   scales[b] = (uint8_t)c;
   if (FP4) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[j] = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[j] |= q[j * 8 + i] << (4 * i);
-    }
     *(uint4*)(codes + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
-    uint32_t w[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      w[j] = q[4 * j] | (q[4 * j + 1] << 8) | (q[4 * j + 2] << 16) | (q[4 * j + 3] << 24);
     *(uint4*)(codes + b * 32) = make_uint4(w[0], w[1], w[2], w[3]);
     *(uint4*)(codes + b * 32 + 16) = make_uint4(w[4], w[5], w[6], w[7]);
   }
@@ -110,7 +105,9 @@ __global__ void __launch_bounds__(256) k_quant_nv(const void* __restrict__ src, 
     if (bsv != 0.0f) {
       const float r = 1.0f / (bsv * g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_encode(v[i] * r) << (4 * (i & 7));
+      for (int h = 0; h < 2; ++h)
+        w[h] = e2m1_x4(v[8 * h] * r, v[8 * h + 1] * r, v[8 * h + 2] * r, v[8 * h + 3] * r) |
+               (e2m1_x4(v[8 * h + 4] * r, v[8 * h + 5] * r, v[8 * h + 6] * r, v[8 * h + 7] * r) << 16);
     }
     scales[row * (cols / 16) + blk] = (uint8_t)bs;
     *(uint2*)(codes + (base + blk * 16) / 2) = make_uint2(w[0], w[1]);
