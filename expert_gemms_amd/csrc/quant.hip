@@ -81,7 +81,19 @@ __global__ void __launch_bounds__(256) k_quant_nv(const void* __restrict__ src, 
     g = fixed_g[row / rows_per_g];
   } else {
     float amax = 0.0f;
-    for (int i = threadIdx.x; i < cols; i += 256) amax = __builtin_fmaxf(amax, __builtin_fabsf(load_elem<F32>(src, base + i)));
+    if constexpr (F32) {
+      for (int i = threadIdx.x; i < cols; i += 256) amax = __builtin_fmaxf(amax, __builtin_fabsf(load_elem<F32>(src, base + i)));
+    } else {
+      // BF16 rows: 8 values (16 bytes) per load
+      for (int i = threadIdx.x * 8; i < cols; i += 256 * 8) {
+        const uint4 u = *(const uint4*)((const uint16_t*)src + base + i);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(u2f(wd[j] << 16)),
+                                                       __builtin_fabsf(u2f(wd[j] & 0xFFFF0000u))));
+      }
+    }
     amax = group_max<6>(amax);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
@@ -93,11 +105,21 @@ __global__ void __launch_bounds__(256) k_quant_nv(const void* __restrict__ src, 
   for (int blk = threadIdx.x; blk < cols / 16; blk += 256) {
     float v[16];
     float amax = 0.0f;
+    if constexpr (F32) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      v[i] = load_elem<F32>(src, base + blk * 16 + i);
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+      for (int i = 0; i < 16; ++i) v[i] = load_elem<F32>(src, base + blk * 16 + i);
+    } else {
+      const uint4* p = (const uint4*)((const uint16_t*)src + base + blk * 16);
+      const uint4 u0 = p[0], u1 = p[1];
+      const uint32_t wd[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[2 * j] = u2f(wd[j] << 16);
+        v[2 * j + 1] = u2f(wd[j] & 0xFFFF0000u);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
     const float t = amax / six_g;
     const uint32_t bs = e4m3_encode(t);
     const float bsv = e4m3_decode(bs);
