@@ -184,12 +184,20 @@ k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, 
                 int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
   __shared__ int wave_tot[DISPATCH_WAVES];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  // the chunks' counts of expert tid, 16 loads in flight at a time (a
+  // load-add-store chain per chunk would wait out each load's latency)
+  constexpr int BATCH = 16;
   int run = 0;
   if (tid < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int n = block_counts[(int64_t)c * E + tid];
-      block_counts[(int64_t)c * E + tid] = run;
-      run += n;
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+      int n[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) n[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = run;
+        run += n[i];
+      }
     }
     counts[tid] = run;
   }
@@ -209,7 +217,14 @@ k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, 
   for (int ww = 0; ww < DISPATCH_WAVES; ++ww) total += wave_tot[ww];
   if (tid < E) {
     offsets[tid] = off;
-    for (int c = 0; c < nchunks; ++c) block_counts[(int64_t)c * E + tid] += off;
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+      int b[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) b[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i)
+        if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = b[i] + off;
+    }
     for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
     for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
   }
