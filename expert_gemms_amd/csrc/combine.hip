@@ -89,14 +89,15 @@ __device__ __forceinline__ void token_sum8(const uint16_t* __restrict__ o16, con
   }
 }
 
-// BF16 slot rows: workgroup (t, c) takes token t, columns [2048 c, 2048 c +
-// 2048), 8 per thread.
-__global__ void __launch_bounds__(256) k_combine16(const uint16_t* __restrict__ o16,
-                                                   const int32_t* __restrict__ slot_row,
-                                                   const float* __restrict__ topk_w, int k, int kk, int H,
-                                                   uint16_t* __restrict__ out) {
+// BF16 slot rows: workgroup (t, c) takes token t, columns [8 B c, 8 B (c + 1))
+// for B = blockDim.x threads, 8 per thread (one workgroup per token up to
+// H = 8192, so no column block is left partly idle).
+__global__ void __launch_bounds__(1024) k_combine16(const uint16_t* __restrict__ o16,
+                                                    const int32_t* __restrict__ slot_row,
+                                                    const float* __restrict__ topk_w, int k, int kk, int H,
+                                                    uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
-  const int h = blockIdx.y * 2048 + threadIdx.x * 8;
+  const int h = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (h >= H) return;
   float acc[8];
   token_sum8(o16, slot_row, topk_w, t, k, kk, H, h, acc);
@@ -182,9 +183,12 @@ void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, con
   else if (gamma)
     hipLaunchKernelGGL(k_combine_norm<false>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
                        slot_row, topk_w, k, kk, H, gamma, eps, out);
-  else if (o_bf16)
-    hipLaunchKernelGGL(k_combine16, dim3(T, (H + 2047) / 2048), dim3(256), 0, stream, (const uint16_t*)o, slot_row,
-                       topk_w, k, kk, H, out);
+  else if (o_bf16) {
+    // H / 8 threads (a multiple of 16, as H is of 128), at most 1024
+    const int threads = H / 8 <= 1024 ? H / 8 : 1024;
+    hipLaunchKernelGGL(k_combine16, dim3(T, (H / 8 + threads - 1) / threads), dim3(threads), 0, stream,
+                       (const uint16_t*)o, slot_row, topk_w, k, kk, H, out);
+  }
   else
     hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
                        out);
