@@ -81,6 +81,7 @@ struct Workspace {
   float* p1;          // K parts of a split L1 GEMM, float32 [ksplit1, S, 2I]
   float* o;           // L2 output rows per slot
   uint16_t* xw;       // BF16 input rows scaled by their routing weight
+  uint16_t* xs;       // BF16: sorted x rows, stage-blocked (the L1 A operand)
   size_t bytes;
 };
 
@@ -98,6 +99,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
   w.block_counts = (int32_t*)take(dispatch_scratch_ints(S, (int)E) * 4);
   w.xq = w.xq_sf = w.a1_sf = w.a2 = w.a2_sf = nullptr;
+  w.xs = nullptr;
   w.x_tok = w.row_tok = nullptr;
   // a scale plane holds every sorted row plus 256 bytes, so a tile's
   // 256-byte plane copy from its first row stays inside
@@ -117,7 +119,10 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
     w.a2 = take(M * I / 2);
     w.a2_sf = take(I / 16 * w.sf_plane);
   } else {
-    w.a2 = take(M * I * 2);
+    // stage-blocked [M / bm][K / 32][bm][32]: whole blocks of bm rows
+    const int64_t Mb = (M + bm - 1) / bm * bm;
+    w.a2 = take(Mb * I * 2);
+    w.xs = (uint16_t*)take(Mb * H * 2);
   }
   w.o = (float*)take(S * H * 4 * ksplit);
   w.p1 = ksplit1 > 1 ? (float*)take(S * 2 * I * 4 * ksplit1) : nullptr;
@@ -460,6 +465,10 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
     launch_gather_sf(w.sorted_slot, w.offsets, E, (int)kk, w.xq_sf, (int)(H / grp), w.sf_plane, M,
                      nv ? 0x38 : 127, w.a1_sf, nv ? w.x_tok : nullptr, w.row_tok, s);
   }
+  if (fmt == MOE_FMT_BF16) {
+    const int64_t M = T * kk + (int64_t)E * (bm - 1);
+    launch_block_rows_bf16((const uint16_t*)xin, w.sorted_slot, w.offsets, E, (int)kk, (int)H, bm, M, w.xs, s);
+  }
   mark(2 * MOE_STEP_DISPATCH + 1);
   const int grid = (d->cus >= 8 ? d->cus : 8) / 8 * 8;
 
@@ -467,8 +476,9 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   const int64_t ebytes = fmt == MOE_FMT_BF16 ? 2 : 1;  // bytes per element (codes); FP4 below
+  g.bm = bm;
   if (fmt == MOE_FMT_BF16) {
-    g.a = (const uint8_t*)xin;
+    g.a = (const uint8_t*)w.xs;   // stage-blocked sorted rows
     g.a_ld = H * 2;
   } else {
     g.a = w.xq;

@@ -339,4 +339,31 @@ void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E,
                      plane, fill, out, a_tok, row_scale);
 }
 
+// BF16 layers: the L1 GEMM's A rows in sorted order and stage-blocked
+// ([M / bm][H / 32][bm][32 values]), so a tile's stage is one contiguous run
+// of full cache lines.  Workgroup m copies sorted row m (x of its token, or
+// zeros for a padding row) in 16-byte chunks.
+__global__ void __launch_bounds__(256) k_block_rows_bf16(const uint16_t* __restrict__ x,
+                                                         const int32_t* __restrict__ sorted_slot,
+                                                         const int32_t* __restrict__ offsets, int E, int kk, int H,
+                                                         int bm, uint16_t* __restrict__ xs) {
+  const int m = blockIdx.x;
+  if (m >= offsets[E]) return;
+  const int sl = sorted_slot[m];
+  const uint16_t* src = x + (int64_t)(sl >= 0 ? sl / kk : 0) * H;
+  uint16_t* dst = xs + (int64_t)(m / bm) * H * bm + (m % bm) * 32;
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    const uint4 v = sl >= 0 ? *(const uint4*)(src + c * 8) : make_uint4(0, 0, 0, 0);
+    // element 8c: stage 8c / 32, column 8c % 32 of that stage's 32
+    *(uint4*)(dst + (int64_t)(c / 4) * bm * 32 + (c % 4) * 8) = v;
+  }
+}
+
+void launch_block_rows_bf16(const uint16_t* x, const int32_t* sorted_slot, const int32_t* offsets, int E, int kk,
+                            int H, int bm, int64_t max_rows, uint16_t* xs, hipStream_t stream) {
+  if (max_rows <= 0) return;
+  hipLaunchKernelGGL(k_block_rows_bf16, dim3((unsigned)max_rows), dim3(256), 0, stream, x, sorted_slot, offsets, E, kk,
+                     H, bm, xs);
+}
+
 }  // namespace moe

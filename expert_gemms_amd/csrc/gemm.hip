@@ -312,8 +312,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // (rows wrap modulo BM when a wave has more lanes than rows).  L1: the
     // wave's A_WROWS contiguous rows' slots come in by scalar loads and each
     // lane picks its rows' token.
+    // BF16: A rows are stage-blocked and already in sorted order
+    constexpr bool BLOCKED = FMT == F_BF16;
     int sv[G::A_WROWS];
-    if constexpr (LAYER != 2) {
+    if constexpr (LAYER != 2 && !BLOCKED) {
       const int32_t* base = p.sorted_slot + t.m0 + (w * G::A_WROWS) % BM;
       if constexpr (G::A_WROWS == 8) {
         const i32x8 v = sload8(base);
@@ -333,7 +335,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
       const int r = rl % BM;
       int64_t row;
-      if constexpr (LAYER != 2) {
+      if constexpr (BLOCKED) {
+        // the tile's block of the [M / BM][K / 32][BM][64 B] layout, row r
+        t.a_off[i] = ((int64_t)(t.m0 / BM) * (p.K / 32) * BM + r) * 64 + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
+        continue;
+      } else if constexpr (LAYER != 2) {
         int sl = sv[i * G::A_RPI];
 #pragma unroll
         for (int k = 1; k < G::A_RPI; ++k)
@@ -355,7 +361,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     constexpr int c = decltype(ci)::value;
     constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
     if constexpr (c < G::A_INSTR) {
-      g2lds16(p.a + t.a_off[c] + (int64_t)(t.s0 + s) * C::A_ROW, st + (w * G::A_INSTR + c) * 1024);
+      constexpr int64_t SSTRIDE = FMT == F_BF16 ? (int64_t)BM * C::A_ROW : C::A_ROW;   // bytes per stage of a row
+      g2lds16(p.a + t.a_off[c] + (int64_t)(t.s0 + s) * SSTRIDE, st + (w * G::A_INSTR + c) * 1024);
     } else if constexpr (c < SC) {
       // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
       // global BF16 [N block][layout stage][32-row block of 8][KS_PER_L

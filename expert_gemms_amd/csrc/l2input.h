@@ -70,7 +70,8 @@ __device__ __forceinline__ void store_l2_input(float a, int64_t row, int icol, i
     if ((l32 & 1) == 0) p.c[row * p.c_ld + (icol >> 1)] = (uint8_t)(q | (qn << 4));
     if ((l32 & 15) == 0) p.c_sf[(int64_t)(icol >> 4) * p.c_sf_ld + row] = (uint8_t)bs;
   } else if constexpr (FMT == F_BF16) {
-    ((uint16_t*)(p.c + row * p.c_ld))[icol] = bf16_rne(a);
+    // stage-blocked: [M / bm][I / 32][bm][32]
+    ((uint16_t*)p.c)[((row / p.bm) * (p.inter / 32) + icol / 32) * p.bm * 32 + (row % p.bm) * 32 + icol % 32] = bf16_rne(a);
   } else {
     const float amax = group_max<5>(__builtin_fabsf(a));
     uint32_t q = 0;
@@ -115,7 +116,9 @@ __device__ __forceinline__ void store_l2_input_rows(const float (&a)[16], int64_
       if (g == h) p.c_sf[(int64_t)((icol0 >> 4) + h) * p.c_sf_ld + row] = (uint8_t)bs;
     }
   } else if constexpr (FMT == F_BF16) {
-    uint16_t* out = (uint16_t*)(p.c + row * p.c_ld) + icol0 + 4 * g;
+    // stage-blocked: [M / bm][I / 32][bm][32]; the 32 columns from icol0 on
+    // are one stage
+    uint16_t* out = (uint16_t*)p.c + ((row / p.bm) * (p.inter / 32) + icol0 / 32) * p.bm * 32 + (row % p.bm) * 32 + 4 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *(uint2*)(out + 8 * j) = make_uint2((uint32_t)bf16_rne(a[4 * j]) | ((uint32_t)bf16_rne(a[4 * j + 1]) << 16),

@@ -53,6 +53,10 @@ struct GemmArgs {
   // L2 of a block-scaled layer with K unsplit: the rows of o are BF16 (RNE of
   // the float32 accumulators), [S, N] uint16
   int o_bf16;
+  // BLOCK_M.  BF16 layers keep both GEMMs' A operand (the sorted x rows, the
+  // L2 input) stage-blocked: [M / bm][K / 32][bm rows][32 values], so a
+  // tile's 32-K stage of A is one contiguous run of bm * 64 bytes
+  int bm;
 };
 
 enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
@@ -86,6 +90,11 @@ void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E,
                       float* row_scale, hipStream_t stream);
 
 void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream);
+
+// BF16 x rows in sorted order, stage-blocked for the L1 GEMM (GemmArgs::bm):
+// sorted row m < offsets[E] takes x[sorted_slot[m] / kk], a padding row zeros.
+void launch_block_rows_bf16(const uint16_t* x, const int32_t* sorted_slot, const int32_t* offsets, int E, int kk,
+                            int H, int bm, int64_t max_rows, uint16_t* xs, hipStream_t stream);
 
 void launch_transform(int fmt, int E, int H, int I, const uint8_t* w13, const uint8_t* w13_sf,
                       const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w13_k, uint8_t* w13_sf_k,
