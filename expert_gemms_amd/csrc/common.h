@@ -48,11 +48,10 @@ __host__ __device__ inline int w13_canonical_row(int n, int inter) {
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// float32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = f2u(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
+// float32 -> bf16 bits, round to nearest even: gfx950's conversion
+// (v_cvt_pk_bf16_f32), the same bits as adding 0x7FFF plus the kept lsb and
+// truncating, for finite inputs.
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // ---------------------------------------------------------------- E4M3 / E2M1
 // Round-to-nearest-even, saturating to the largest finite magnitude; the
