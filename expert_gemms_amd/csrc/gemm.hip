@@ -289,6 +289,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     int par;                // its row buffer
     int64_t a_off[G::A_INSTR];
     const uint8_t* wexp;
+    const uint8_t* wbase;   // the tile's N block of the weights (layout stage 0)
     const uint8_t* wsf;
   };
   auto make_tile = [&](int uu) __attribute__((always_inline)) -> TileCtx {
@@ -351,6 +352,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       t.a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
     }
     t.wexp = p.w + (int64_t)e * p.w_expert_bytes;
+    {
+      constexpr int LSK = C::KSTAGE / C::STEPS * C::KS_PER_L;   // K per layout stage
+      t.wbase = t.wexp + (FMT == F_BF16 ? (int64_t)t.nb * (p.K / LSK) * 8 * (C::KS_PER_L * C::FRAG)
+                                        : (int64_t)t.nb * 8 * (C::KS_PER_L * C::FRAG));
+    }
     t.wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
     return t;
   };
@@ -367,15 +373,19 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
       // global BF16 [N block][layout stage][32-row block of 8][KS_PER_L
       // K-steps][FRAG], others [layout stage][32-row block][KS_PER_L][FRAG]
+      // the tile's weight base (t.wbase), a term per stage (layout stage
+      // S / R of the tile's N block, K-step (S % R) * STEPS within it) and a
+      // term per copy (32-row block nf, K-step ksl of the stage, 1 KiB piece)
       const int q = w * G::B_INSTR + (c - G::A_INSTR);
       const int nf = q / G::B_FRAGS_PER_NF, piece = q % G::B_FRAGS_PER_NF;
       const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
-      const int kg = (t.s0 + s) * C::STEPS + ksl;
-      constexpr int LSK = C::KSTAGE / C::STEPS * C::KS_PER_L;   // K per layout stage
-      const int64_t blk = FMT == F_BF16 ? ((int64_t)t.nb * (p.K / LSK) + kg / C::KS_PER_L) * 8 + nf
-                                        : (int64_t)(kg / C::KS_PER_L) * (p.N / 32) + t.nb * 8 + nf;
-      const uint8_t* src = t.wexp + blk * (C::KS_PER_L * C::FRAG) + (kg % C::KS_PER_L) * C::FRAG + sub * 1024 + lane * 16;
-      g2lds16(src, st + G::A_STAGE + q * 1024);
+      constexpr unsigned R = C::KS_PER_L / C::STEPS;   // kernel stages per layout stage
+      const unsigned S = (unsigned)(t.s0 + s);
+      const int64_t lstride = FMT == F_BF16 ? (int64_t)8 * C::KS_PER_L * C::FRAG
+                                            : (int64_t)(p.N / 32) * (C::KS_PER_L * C::FRAG);
+      const int64_t sterm = (int64_t)(S / R) * lstride + (int64_t)((S % R) * (C::STEPS * C::FRAG));
+      const int cterm = nf * (C::KS_PER_L * C::FRAG) + ksl * C::FRAG + sub * 1024;
+      g2lds16(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
       // A scales: K block w % (blocks per stage) of this stage, the plane's
       // bytes of rows m0 .. m0+255 (rows past the tile are not read)
