@@ -291,6 +291,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     const uint8_t* wexp;
     const uint8_t* wbase;   // the tile's N block of the weights (layout stage 0)
     const uint8_t* wsf;
+    const uint8_t* asf;     // MX: the wave's A-scale plane at the tile's first row (stage 0)
+    const uint8_t* bsf;     // MX: the wave's B-scale column blocks (layout stage 0)
   };
   auto make_tile = [&](int uu) __attribute__((always_inline)) -> TileCtx {
     TileCtx t;
@@ -358,6 +360,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
                                         : (int64_t)t.nb * 8 * (C::KS_PER_L * C::FRAG));
     }
     t.wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
+    if constexpr (C::SCALED && !C::NV) {
+      t.asf = p.a_sf + t.m0 + (int64_t)(w % (C::KSTAGE / 32)) * p.a_sf_ld;
+      t.bsf = t.wsf + (int64_t)(t.nb * 8 + 2 * w) * 128;
+    }
     return t;
   };
 
@@ -389,15 +395,18 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     } else if constexpr (!C::NV && c == SC) {
       // A scales: K block w % (blocks per stage) of this stage, the plane's
       // bytes of rows m0 .. m0+255 (rows past the tile are not read)
-      constexpr int NBLK = C::KSTAGE / 32;
-      const int64_t blk = (int64_t)(t.s0 + s) * NBLK + w % NBLK;
-      __builtin_amdgcn_global_load_lds(p.a_sf + blk * p.a_sf_ld + t.m0 + lane * 4,
+      // (the tile's base t.asf plus NBLK planes per stage; plane strides fit
+      // 32 bits)
+      constexpr unsigned NBLK = C::KSTAGE / 32;
+      const uint64_t soff = (uint64_t)(unsigned)(t.s0 + s) * (NBLK * (unsigned)p.a_sf_ld);
+      __builtin_amdgcn_global_load_lds(t.asf + soff + lane * 4,
                                        (lds_void*)(st + G::A_STAGE + G::B_STAGE + w * 256), 4, 0, 0);
     } else if constexpr (!C::NV) {
       // B scales: [layout stage][32-row block][64 lanes x 2 K-steps]; wave w
       // copies column blocks 2w and 2w + 1 (256 contiguous bytes)
-      const uint8_t* src = t.wsf + ((int64_t)((t.s0 + s) / G::SPL) * (p.N / 32) + t.nb * 8 + 2 * w) * 128 + lane * 4;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 256), 4, 0,
+      const uint64_t soff = (uint64_t)((unsigned)(t.s0 + s) / G::SPL) * ((unsigned)(p.N / 32) * 128u);
+      __builtin_amdgcn_global_load_lds(t.bsf + soff + lane * 4,
+                                       (lds_void*)(st + G::A_STAGE + G::B_STAGE + G::A_SF_STAGE + w * 256), 4, 0,
                                        0);
     } else if constexpr (c < SC + 2) {
       // NVFP4 A scales: K blocks w and w + 4 of this stage's 8, the planes'
