@@ -17,7 +17,8 @@
 namespace moe {
 
 // Columns h .. h+3 of slot row s: float32 rows (with K split, the parts
-// added in part order) or BF16 rows (one part).
+// added in part order) or BF16 rows (one part).  Slot rows are read once, so
+// their loads are non-temporal.
 template <bool O16>
 __device__ __forceinline__ f32x4 slot_cols(const float* __restrict__ o, int nsplit, int64_t o_split, int64_t s,
                                            int H, int h) {
@@ -25,8 +26,8 @@ __device__ __forceinline__ f32x4 slot_cols(const float* __restrict__ o, int nspl
     const uint2 b = *(const uint2*)((const uint16_t*)o + s * H + h);
     return (f32x4){u2f(b.x << 16), u2f(b.x & 0xFFFF0000u), u2f(b.y << 16), u2f(b.y & 0xFFFF0000u)};
   } else {
-    f32x4 v = *(const f32x4*)(o + s * H + h);
-    for (int q = 1; q < nsplit; ++q) v += *(const f32x4*)(o + q * o_split + s * H + h);
+    f32x4 v = __builtin_nontemporal_load((const f32x4*)(o + s * H + h));
+    for (int q = 1; q < nsplit; ++q) v += __builtin_nontemporal_load((const f32x4*)(o + q * o_split + s * H + h));
     return v;
   }
 }
@@ -74,7 +75,10 @@ __device__ __forceinline__ void token_sum8(const uint16_t* __restrict__ o16, con
     uint4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (j0 + i < kk) v[i] = *(const uint4*)(o16 + (s0 + j0 + i) * H + h);
+      if (j0 + i < kk) {
+        const i32x4 q = __builtin_nontemporal_load((const i32x4*)(o16 + (s0 + j0 + i) * H + h));
+        v[i] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

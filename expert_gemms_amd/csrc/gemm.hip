@@ -724,7 +724,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         }
       }
       // block-scaled L2 with K unsplit: BF16 rows (the output dtype the
-      // combine reads); else float32 rows (BF16 layers, K parts, split L1)
+      // combine reads), stored non-temporally (written once, read once by
+      // the combine, so they need not displace the weights from the
+      // caches); else float32 rows (BF16 layers, K parts, split L1)
       const bool o16 = FMT != F_BF16 && LAYER == 2 && p.o_bf16;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -736,7 +738,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           if (o16) {
             uint16_t* orow = (uint16_t*)p.o + col;
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]);
+            for (int tn = 0; tn < TN; ++tn)
+              __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]), orow + tn * 32);
           } else {
             float* orow = p.o + ta.ks * p.o_split + col;
 #pragma unroll
