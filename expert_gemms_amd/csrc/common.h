@@ -204,4 +204,10 @@ __device__ __forceinline__ void g2lds16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// The same copy with the non-temporal cache policy (the `nt` bit): for data
+// that one workgroup reads once and no other is about to read.
+__device__ __forceinline__ void g2lds16_nt(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 2);
+}
+
 }  // namespace moe

@@ -391,7 +391,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
                                             : (int64_t)(p.N / 32) * (C::KS_PER_L * C::FRAG);
       const int64_t sterm = (int64_t)(S / R) * lstride + (int64_t)((S % R) * (C::STEPS * C::FRAG));
       const int cterm = nf * (C::KS_PER_L * C::FRAG) + ksl * C::FRAG + sub * 1024;
-      g2lds16(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
+      // 32-row tiles (the BLOCK_M of decode-sized batches, where an expert
+      // rarely has more than one M block) stream their weights: each line is
+      // read by one workgroup once, so it is copied non-temporally and does
+      // not displace lines that are still to be read.  Taller tiles share
+      // weight blocks between an expert's M blocks and keep them cached.
+      if constexpr (BM <= 32)
+        g2lds16_nt(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
+      else
+        g2lds16(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
       // A scales: K block w % (blocks per stage) of this stage, the plane's
       // bytes of rows m0 .. m0+255 (rows past the tile are not read)
