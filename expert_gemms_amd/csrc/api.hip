@@ -447,15 +447,24 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
     launch_scale_rows((const uint16_t*)x, topk_weights, num_tokens, (int)H, w.xw, s);
     xin = w.xw;
   }
-  if (fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4)
+  // MX formats with the single-workgroup dispatch: quantisation and routing
+  // metadata (a2) in one launch, timed as the quantisation step
+  const bool mx = fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4;
+  const bool fused = mx && (!w.block_counts || dispatch_single_wg(num_tokens, top_k, num_shared));
+  if (fused)
+    launch_dispatch_quant_mx(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts,
+                             w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, xin, (int)H, w.xq,
+                             w.xq_sf, s);
+  else if (mx)
     launch_quant_mx(false, false, T, (int)H, xin, w.xq, w.xq_sf, s);
   else if (fmt == MOE_FMT_NVFP4)
     launch_quant_nv(false, T, (int)H, xin, w.xq, w.xq_sf, w.x_tok, nullptr, 1, s);
   mark(2 * MOE_STEP_QUANT_X + 1);
   // a2: routing metadata
   mark(2 * MOE_STEP_DISPATCH);
-  launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts, w.offsets,
-                  w.sorted_slot, w.slot_row, w.tile_expert, w.meta, w.block_counts, s);
+  if (!fused)
+    launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts,
+                    w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, w.block_counts, s);
   const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
   const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (scaled) {

@@ -17,6 +17,7 @@
 // Pass 3 walks the batches again in order and scatters every slot to
 // offset + (earlier slots of its expert), which is the stable order.
 #include "common.h"
+#include "l2input.h"
 #include "launch.h"
 
 namespace moe {
@@ -81,11 +82,11 @@ __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ topk_id
   }
 }
 
-__global__ void __launch_bounds__(DISPATCH_THREADS)
-k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc,
-           int bm, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-           int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
-           int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+__device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start,
+                                            int n_loc, int bm, int nbits, int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+                                            int32_t* __restrict__ slot_row, int32_t* __restrict__ tile_expert,
+                                            int32_t* __restrict__ meta) {
   __shared__ int hist[DISPATCH_WAVES][MAX_LOCAL_EXPERTS];
   __shared__ int wave_tot[DISPATCH_WAVES];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
@@ -145,6 +146,34 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
     for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
     for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
   }
+}
+
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc,
+           int bm, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+           int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+           int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+  dispatch_wg(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert,
+              meta);
+}
+
+// The single-workgroup dispatch and the MX dispatch quantisation of x (E4M3
+// codes, BF16 input) in one launch: the two are independent, so workgroup 0
+// builds the routing metadata while workgroups 1 .. quantise x, one MX block
+// per thread; this saves a launch on decode-sized batches.
+__global__ void __launch_bounds__(DISPATCH_THREADS)
+k_dispatch_quant_mx(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+                    int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
+                    int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta, const void* __restrict__ x,
+                    int64_t nblocks, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  if (blockIdx.x == 0) {
+    dispatch_wg(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert,
+                meta);
+    return;
+  }
+  const int64_t b = (int64_t)(blockIdx.x - 1) * DISPATCH_THREADS + threadIdx.x;
+  if (b < nblocks) quant_mx_block<false, false>(x, b, codes, scales);
 }
 
 // Many-workgroup dispatch for large slot counts: the same metadata in three
@@ -284,6 +313,22 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
   }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh, start,
                      n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta);
+}
+
+bool dispatch_single_wg(int T, int k, int n_sh) { return (int64_t)T * (k + n_sh) < DISPATCH_MANY_MIN_SLOTS; }
+
+void launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+                              int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                              int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  const int E = n_loc + n_sh;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int64_t nblocks = (int64_t)T * (H / 32);
+  const unsigned nq = (unsigned)((nblocks + DISPATCH_THREADS - 1) / DISPATCH_THREADS);
+  hipLaunchKernelGGL(k_dispatch_quant_mx, dim3(1 + nq), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh,
+                     start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta, x, nblocks,
+                     codes, scales);
 }
 
 // Block scales of the L1 A operand in the GEMM's layout: one plane per

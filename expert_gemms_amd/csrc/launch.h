@@ -69,6 +69,14 @@ int64_t dispatch_scratch_ints(int64_t S, int E);
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
                      int32_t* tile_expert, int32_t* meta, int32_t* block_counts, hipStream_t stream);
+// True when launch_dispatch runs the single-workgroup kernel.
+bool dispatch_single_wg(int T, int k, int n_sh);
+// That kernel and the MX dispatch quantisation of BF16 x [T, H] (E4M3 codes,
+// UE8M0 scales, as launch_quant_mx(false, false, ...)) in one launch.
+void launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+                              int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
+                              int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
 
 // Sum of the K parts of a split L1 GEMM (a.o, a.ksplit, a.o_split), then its
 // activation and L2-input quantisation into (a.c, a.c_sf).

@@ -15,53 +15,12 @@
 
 namespace moe {
 
-template <bool F32>
-__device__ __forceinline__ float load_elem(const void* src, int64_t i) {
-  if (F32) return ((const float*)src)[i];
-  uint32_t b = (uint32_t)((const uint16_t*)src)[i] << 16;
-  return u2f(b);
-}
-
-// One thread per 32-element MX block.  Element codes are written unpacked
-// for E4M3 and two per byte for E2M1, by the hardware converts (equal to the
-// software encoders here: the scaled block maximum is at most the format's
-// largest value).
+// One thread per 32-element MX block (the block body is quant_mx_block).
 template <bool F32, bool FP4>
 __global__ void __launch_bounds__(256) k_quant_mx(const void* __restrict__ src, int64_t nblocks,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-#pragma clang fp contract(off)
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  float v[32];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = load_elem<F32>(src, b * 32 + i);
-    amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-  }
-  int c = 0;
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (amax > 0.0f) {
-    c = mx_scale_code<FP4>(amax);
-    float x[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = __builtin_ldexpf(v[i], 127 - c);
-#pragma unroll
-    for (int j = 0; j < (FP4 ? 4 : 8); ++j) {
-      if constexpr (FP4)
-        w[j] = e2m1_x4(x[8 * j], x[8 * j + 1], x[8 * j + 2], x[8 * j + 3]) |
-               (e2m1_x4(x[8 * j + 4], x[8 * j + 5], x[8 * j + 6], x[8 * j + 7]) << 16);
-      else
-        w[j] = e4m3_x4_mx(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
-    }
-  }
-  scales[b] = (uint8_t)c;
-  if (FP4) {
-    *(uint4*)(codes + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    *(uint4*)(codes + b * 32) = make_uint4(w[0], w[1], w[2], w[3]);
-    *(uint4*)(codes + b * 32 + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  }
+  if (b < nblocks) quant_mx_block<F32, FP4>(src, b, codes, scales);
 }
 
 // NVFP4: one workgroup per row.  The row's global scale is either given
