@@ -8,15 +8,23 @@ GEMM + SwiGLU + L2-input quantisation, L2 GEMM, weighted combine) over one
 batch of synthetic input already resident in HBM.  W untimed warm-up steps,
 then exactly K steps between two synchronisations; one JSON line on stdout.
 
-Default workload: the Mixtral-8x7B-shaped BF16 layer (4096 tokens, hidden
-4096, intermediate 14336, 8 experts, top-2).  --config picks another seeded
-workload (tiny_bf16, mixtral_bf16, dsv3_mxfp8, decode_mxfp4, nvfp4_zipf).
+Default: every format's seeded workload in one run, one JSON line.  Its
+headline is the largest single-GPU layer, DeepSeek-V3-shaped MXFP8 (8192
+tokens, hidden 7168, intermediate 2048, 256 routed experts + 1 shared,
+top-8); ``workloads`` holds one record of the same form per other workload:
+Mixtral-8x7B-shaped BF16 (4096 tokens), the NVFP4 layer under Zipf routing
+(16384 tokens), and the decode-shaped MXFP4 (W4A8) layer at 1, 8, 32, 128
+and 256 tokens, each decode step timed after a 1 GiB read that evicts the
+256 MB MALL.  --config runs one workload alone.
 
-Roofline: the dominant kernel is timed live with HIP events recorded by the
-library on the stream it launches on (moe_forward_profiled).  Its algorithmic
-work is 4 * S * H * I FLOPs for the L1 GEMM (S real slots; padding rows are
-overhead) or the weight bytes it must stream, against MI355X's published
-peaks (dense MFMA BF16 2500 TFLOP/s, FP8 5000; HBM 8000 GB/s).
+Roofline: the dominant kernel (the L1 grouped GEMM) is timed live with HIP
+events recorded by the library on the stream it launches on
+(moe_forward_profiled).  Its algorithmic work is 4 * S * H * I FLOPs (S real
+slots; padding rows are overhead) or the weight bytes it must stream,
+against MI355X's published peaks (dense MFMA BF16/FP16 2500 TFLOP/s, FP8
+5000, FP4 10100; HBM 8000 GB/s).  NVFP4 runs its products on the FP16 MFMA
+(exactly dequantised operands), so its fraction is of the FP16 peak, with
+the FP4 peak's fraction alongside.
 """
 
 import argparse
@@ -32,7 +40,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 5000.0, "nvfp4": 2500.0}
+PEAK_FP4_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
+HEADLINE = ("dsv3_mxfp8", None, 0)
+# (workload, tokens, MB read between steps)
+SUB_WORKLOADS = [("mixtral_bf16", None, 0), ("nvfp4_zipf", None, 0)] + \
+    [("decode_mxfp4", t, 1024) for t in (1, 8, 32, 128, 256)]
 
 
 def parse():
@@ -40,7 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", default="mixtral_bf16")
+    p.add_argument("--config", default=None, help="one workload alone (default: every workload)")
     p.add_argument("--tokens", type=int, default=None, help="token count (decode workload)")
     p.add_argument("--flush-mb", type=int, default=0,
                    help="read this many MB between steps (evicts the weights from the 256 MB MALL without "
@@ -115,19 +128,15 @@ def scale_bytes_per_elem(fmt):
     return {"bf16": 0.0, "mxfp8": 1 / 32, "mxfp4": 1 / 32, "nvfp4": 1 / 16}[fmt]
 
 
-def build_layer(cfg, T, device):
-    """Seeded inputs on the device, weights quantised by the library's own
-    quantiser and transformed to the kernel layout."""
+def build_weights(cfg, device, max_tokens):
+    """Weights drawn on the device, quantised by the library's own quantiser
+    and transformed to the kernel layout, in a layer sized for max_tokens."""
     import expert_gemms_amd as moe
-    from synth import gen_x_bf16, gen_routing, gen_weight_f32_device, gen_w2_input_scale
+    from synth import gen_weight_f32_device, gen_w2_input_scale
 
     fmt = cfg.fmt
     E = cfg.E + cfg.num_shared
     H, I = cfg.H, cfg.I
-    x = gen_x_bf16(cfg, T).to(device)
-    ids, wts = gen_routing(cfg, T)
-    ids_d = torch.from_numpy(ids).to(device)
-    wts_d = torch.from_numpy(wts).to(device)
     vpe = 2 if fmt in ("mxfp4", "nvfp4") else 1
     grp = 16 if fmt == "nvfp4" else 32
     canon = {}
@@ -149,12 +158,20 @@ def build_layer(cfg, T, device):
             canon[name], canon[name + "_sf"] = codes, sf
             if gs is not None:
                 canon[name + "_gs"] = gs
-    layer = moe.FusedMoE(fmt, H, I, cfg.E, cfg.top_k, num_shared=cfg.num_shared, max_tokens=T)
+    layer = moe.FusedMoE(fmt, H, I, cfg.E, cfg.top_k, num_shared=cfg.num_shared, max_tokens=max_tokens)
     w2_in = torch.from_numpy(gen_w2_input_scale(cfg)) if fmt == "nvfp4" else None
     layer.load_canonical(canon["w13"], canon["w2"], canon.get("w13_sf"), canon.get("w2_sf"),
                          canon.get("w13_gs"), canon.get("w2_gs"), w2_input_scale=w2_in)
     torch.cuda.synchronize()
-    return layer, x, ids, wts, ids_d, wts_d, canon
+    return layer, canon
+
+
+def build_inputs(cfg, T, device):
+    """Seeded x (BF16) and routing of T tokens, on the device and the host."""
+    from synth import gen_x_bf16, gen_routing
+    x = gen_x_bf16(cfg, T).to(device)
+    ids, wts = gen_routing(cfg, T)
+    return x, ids, wts, torch.from_numpy(ids).to(device), torch.from_numpy(wts).to(device)
 
 
 def algorithmic(cfg, T, ids):
@@ -201,9 +218,38 @@ def cpu_baseline(cfg, T, x, ids, wts, canon, n_tok, min_seconds=10.0):
     flops = 6.0 * S * cfg.H * cfg.I
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     touched = np.unique(ids[:n_tok][(ids[:n_tok] >= 0) & (ids[:n_tok] < cfg.E)]).size + cfg.num_shared
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    host = host_cpu()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(threads, host["usable_cpus"])),
+            "kind": "oracle", "blas_threads": int(threads), "physical_cores": host["physical_cores"],
+            "usable_cpus": host["usable_cpus"], "cpu_model": host["model"],
             "sample": f"first {n_tok} of {T} tokens of the same workload ({S} slots, {touched} experts "
                       f"dequantised per pass); {passes} pass(es), {dt:.2f} s per pass"}
+
+
+def host_cpu():
+    """CPU model, physical cores of the host and CPUs this process may use."""
+    model, cores = "unknown", set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name":
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return {"model": model, "physical_cores": len(cores) or None, "usable_cpus": usable}
 
 
 def default_cpu_tokens(cfg, T):
@@ -279,27 +325,17 @@ def route_bench(args, cfg, T):
     return 0
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer's expert-parallel path across GPUs is not built)", file=sys.stderr)
-        return 2
-    if args.copy_mb:
-        return copy_calibration(args.copy_mb)
-    from synth import CONFIGS
+def time_workload(args, cfg, T, flush_mb, layer, canon, min_cpu_seconds):
+    """One workload: warm-up, K timed steps, per-step kernel times, the
+    percentiles, a graph replay, the roofline of the L1 GEMM and the oracle
+    beside it.  Returns the record."""
     import expert_gemms_amd as moe
 
-    cfg = CONFIGS[args.config]
-    T = args.tokens if args.tokens is not None else cfg.T
     device = torch.device("cuda:0")
-    torch.cuda.set_device(device)
-    if args.route:
-        return route_bench(args, cfg, T)
-    layer, x, ids, wts, ids_d, wts_d, canon = build_layer(cfg, T, device)
+    x, ids, wts, ids_d, wts_d = build_inputs(cfg, T, device)
     out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=device)
     stream = torch.cuda.current_stream()
-    flush = torch.ones(args.flush_mb * (1 << 18), dtype=torch.int32, device=device) if args.flush_mb else None
+    flush = torch.ones(flush_mb * (1 << 18), dtype=torch.int32, device=device) if flush_mb else None
     flush_sink = torch.zeros((), dtype=torch.int64, device=device)
 
     def evict():
@@ -313,13 +349,15 @@ def main():
             e.record(stream)          # creates the underlying hipEvent
         return evs
 
+    fwd = lambda: layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
     for _ in range(args.warmup):
-        layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
+        if flush is not None:
+            evict()
+        fwd()
     torch.cuda.synchronize()
 
-    # timed: K plain steps (with --flush-mb, each step is timed on its own so
+    # timed: K plain steps (with a flush, each step is timed on its own so
     # the flush stays outside)
-    fwd = lambda: layer.forward(x, ids_d, wts_d, out=out, block_m=args.block_m)
     wall0 = time.perf_counter()
     if flush is None:
         t_start = torch.cuda.Event(enable_timing=True)
@@ -386,6 +424,7 @@ def main():
         g1.record(stream)
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
+        del g
 
     flops, hbm_bytes, l1_flops, l1_wbytes, touched = algorithmic(cfg, T, ids)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -397,6 +436,9 @@ def main():
         achieved = l1_flops / (l1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": "L1 grouped GEMM"}
+        if cfg.fmt == "nvfp4":
+            roof["peak_note"] = "FP16 MFMA (exactly dequantised NVFP4 operands)"
+            roof["frac_of_fp4_peak"] = round(achieved / PEAK_FP4_TFLOPS, 4)
     else:
         achieved = l1_wbytes / (l1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -412,9 +454,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or default_cpu_tokens(cfg, T)
-        cpu = cpu_baseline(cfg, T, x, ids, wts, canon, n_tok)
+        cpu = cpu_baseline(cfg, T, x, ids, wts, canon, n_tok, min_seconds=min_cpu_seconds)
 
     S = T * (cfg.top_k + cfg.num_shared)
+    mfma_frac = tflops / peak
     rec = {
         "metric": "MoE-layer TFLOP/s (HBM GB/s alongside; fraction of MI355X peak) per format",
         "value": round(tflops, 2),
@@ -430,11 +473,10 @@ def main():
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg.name, "format": cfg.fmt, "tokens": T, "hidden": cfg.H, "inter": cfg.I,
                    "experts": cfg.E, "shared": cfg.num_shared, "top_k": cfg.top_k, "slots": S,
-                   "touched_experts": int(touched), "block_m": bm,
-                   "flush_mb": args.flush_mb},
+                   "touched_experts": int(touched), "block_m": bm, "flush_mb": flush_mb},
         "hbm_gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "mfma_frac": round(tflops / peak, 4),
+        "mfma_frac": round(mfma_frac, 4),
         "step_ms": {k: round(v, 4) for k, v in per_step.items()},
         "step_ms_p10_p50_p90": [step_pct[10], step_pct[50], step_pct[90]],
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
@@ -442,7 +484,53 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
+    if cfg.fmt == "nvfp4":
+        rec["mfma_frac_of_fp4_peak"] = round(tflops / PEAK_FP4_TFLOPS, 4)
+    del out, flush
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer's expert-parallel path across GPUs is not built)", file=sys.stderr)
+        return 2
+    if args.copy_mb:
+        return copy_calibration(args.copy_mb)
+    from synth import CONFIGS
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    if args.config is not None:
+        cfg = CONFIGS[args.config]
+        T = args.tokens if args.tokens is not None else cfg.T
+        if args.route:
+            return route_bench(args, cfg, T)
+        layer, canon = build_weights(cfg, device, T)
+        rec = time_workload(args, cfg, T, args.flush_mb, layer, canon, 10.0)
+        print(json.dumps(rec), flush=True)
+        return 0
+
+    # every workload; the weights of one workload are built once for all its
+    # token counts and freed before the next workload
+    plan = [HEADLINE] + SUB_WORKLOADS
+    recs, built = [], (None, None, None)
+    for i, (name, tokens, flush_mb) in enumerate(plan):
+        cfg = CONFIGS[name]
+        T = tokens if tokens is not None else cfg.T
+        if built[0] != name:
+            built = (None, None, None)
+            torch.cuda.empty_cache()
+            max_t = max((t if t is not None else cfg.T) for n, t, _ in plan if n == name)
+            layer, canon = build_weights(cfg, device, max_t)
+            built = (name, layer, canon)
+        _, layer, canon = built
+        print(f"bench: {name} T={T}", file=sys.stderr, flush=True)
+        recs.append(time_workload(args, cfg, T, flush_mb, layer, canon, 10.0 if i == 0 else 5.0))
+    head = recs[0]
+    head["workloads"] = recs[1:]
+    print(json.dumps(head), flush=True)
     return 0
 
 

@@ -250,6 +250,43 @@ int l1_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
   return best;
 }
 
+// The checks of moe_forward on the layer's shape (no pointers): MOE_OK or
+// MOE_E_INVALID.
+int check_shape(int fmt, int num_tokens, int hidden, int inter, int top_k, int num_local_experts, int num_shared,
+                int block_m) {
+  if (!valid_fmt(fmt)) return MOE_E_INVALID;
+  if (num_tokens < 0 || hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128) return MOE_E_INVALID;
+  if (top_k < 1 || num_local_experts < 1 || num_shared < 0 || num_local_experts + num_shared > MAX_LOCAL_EXPERTS)
+    return MOE_E_INVALID;
+  if ((int64_t)num_tokens * (top_k + num_shared) > (int64_t)1 << 30) return MOE_E_INVALID;
+  if (block_m != 0 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return MOE_E_INVALID;
+  return MOE_OK;
+}
+
+// BLOCK_M, K splits and workspace carve-up of one forward call (host only):
+// the rule's BLOCK_M when block_m is 0; the K splits the rules pick, each
+// dropped (L1 first) while the workspace cannot hold its float32 parts.
+struct Resolved {
+  int bm, ks, ks1;
+  Workspace w;
+};
+int resolve(int fmt, int num_tokens, int hidden, int inter, int top_k, int num_local_experts, int num_shared,
+            int block_m, size_t workspace_bytes, uint8_t* base, Resolved* r) {
+  const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
+  const int64_t T = num_tokens, H = hidden, I = inter;
+  int ks = l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  int ks1 = l1_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  auto need = [&]() { return plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, nullptr).bytes; };
+  if (need() > workspace_bytes) ks1 = 1;
+  if (need() > workspace_bytes) ks = 1;
+  if (need() > workspace_bytes) return MOE_E_WORKSPACE;
+  r->bm = bm;
+  r->ks = ks;
+  r->ks1 = ks1;
+  r->w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, base);
+  return MOE_OK;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   g_last_hip = e;
@@ -386,6 +423,47 @@ int moe_route(int num_tokens, int num_experts, int top_k, const float* logits, c
   return hip_status(hipGetLastError());
 }
 
+int64_t moe_dispatch_scratch_ints(int num_tokens, int top_k, int num_shared, int num_local_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_shared < 0 || num_local_experts < 1) return -1;
+  return dispatch_scratch_ints((int64_t)num_tokens * (top_k + num_shared), num_local_experts + num_shared);
+}
+
+int moe_workspace_layout(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int num_local_experts,
+                         int num_shared, int block_m, size_t workspace_bytes, moe_workspace_layout_t* layout) {
+  if (!layout) return MOE_E_INVALID;
+  const int sst = check_shape(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m);
+  if (sst != MOE_OK) return sst;
+  Resolved rs;
+  // carve from a non-null base so that absent buffers stay distinguishable
+  uint8_t* const base = (uint8_t*)(uintptr_t)4096;
+  const int rst = resolve(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m,
+                          workspace_bytes, base, &rs);
+  if (rst != MOE_OK) return rst;
+  auto off = [&](const void* p) -> int64_t { return p ? (int64_t)((const uint8_t*)p - base) : -1; };
+  const Workspace& w = rs.w;
+  moe_workspace_layout_t& L = *layout;
+  L.block_m = rs.bm;
+  L.l1_ksplit = rs.ks1;
+  L.l2_ksplit = rs.ks;
+  L.l2_rows_bf16 = fmt != MOE_FMT_BF16 && rs.ks == 1;
+  L.sf_plane = fmt == MOE_FMT_BF16 ? 0 : w.sf_plane;
+  L.a2_ld = fmt == MOE_FMT_BF16 ? (int64_t)inter * 2 : (fmt == MOE_FMT_NVFP4 ? inter / 2 : inter);
+  L.counts = off(w.counts);
+  L.offsets = off(w.offsets);
+  L.sorted_slot = off(w.sorted_slot);
+  L.slot_row = off(w.slot_row);
+  L.tile_expert = off(w.tile_expert);
+  L.xq = off(w.xq);
+  L.xq_sf = off(w.xq_sf);
+  L.x_tok = off(w.x_tok);
+  L.a1_sf = off(w.a1_sf);
+  L.a2 = off(w.a2);
+  L.a2_sf = off(w.a2_sf);
+  L.o = off(w.o);
+  L.bytes = (int64_t)w.bytes;
+  return MOE_OK;
+}
+
 int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
                          int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
                          const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
@@ -393,12 +471,8 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
                          const float* w2_gscale, float l2_activation_scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* ev) {
   // ---- shapes and parameters
-  if (!valid_fmt(fmt)) return MOE_E_INVALID;
-  if (num_tokens < 0 || hidden <= 0 || inter <= 0 || hidden % 128 || inter % 128) return MOE_E_INVALID;
-  if (top_k < 1 || num_local_experts < 1 || num_shared < 0 || num_local_experts + num_shared > MAX_LOCAL_EXPERTS)
-    return MOE_E_INVALID;
-  if ((int64_t)num_tokens * (top_k + num_shared) > (int64_t)1 << 30) return MOE_E_INVALID;
-  if (block_m != 0 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return MOE_E_INVALID;
+  const int shape_status = check_shape(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m);
+  if (shape_status != MOE_OK) return shape_status;
   moe_activation_t a = {MOE_ACT_SWIGLU, 0, 0.0f, 1.0f, 0.0f};
   if (act) a = *act;
   if (a.kind != MOE_ACT_SWIGLU) return MOE_E_UNSUPPORTED;
@@ -421,20 +495,18 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   if (scaled && (!w13_sf_k || !w2_sf_k || !aligned16(w13_sf_k) || !aligned16(w2_sf_k))) return MOE_E_INVALID;
   if (fmt == MOE_FMT_NVFP4 && (!w13_gscale || !w2_gscale)) return MOE_E_INVALID;
   if (!gemm_fmt(fmt) || hidden % 256) return MOE_E_UNSUPPORTED;
-  const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
+  Resolved rs;
+  const int rst = resolve(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m,
+                          workspace_bytes, (uint8_t*)workspace, &rs);
+  if (rst != MOE_OK) return rst;
+  const int bm = rs.bm, ks = rs.ks, ks1 = rs.ks1;
+  const Workspace& w = rs.w;
   const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
   const int E = num_local_experts + num_shared;
-  int ks = l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  int ks1 = l1_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  auto need = [&]() { return plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, nullptr).bytes; };
-  if (need() > workspace_bytes) ks1 = 1;
-  if (need() > workspace_bytes) ks = 1;
-  if (need() > workspace_bytes) return MOE_E_WORKSPACE;
   DeviceInfo* d;
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  Workspace w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, (uint8_t*)workspace);
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
   };

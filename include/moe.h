@@ -152,6 +152,13 @@ int moe_quantize_weights(moe_format_t fmt, int num_experts, int rows, int cols,
 int moe_quantize_x(moe_format_t fmt, int num_tokens, int hidden, const void* x,
                    void* codes, void* scales, float* token_scale, void* stream);
 
+/* Size, in int32 values, of moe_dispatch's optional block_counts scratch
+ * for num_tokens tokens: ceil(S / 2048) * E' with S = num_tokens * (top_k +
+ * num_shared) slots and E' = num_local_experts + num_shared.  Returns -1 on
+ * invalid arguments (negative counts, top_k < 1, num_local_experts < 1).
+ * Host-only. */
+int64_t moe_dispatch_scratch_ints(int num_tokens, int top_k, int num_shared, int num_local_experts);
+
 /* Router top-k: float32 router logits [T, E] (device) -> topk_ids int32
  * [T, top_k] and topk_weights float32 [T, top_k] (device), the input
  * moe_forward takes.  The routing the "fused_moe" page's
@@ -265,6 +272,44 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
                          float l2_activation_scale,
                          void* out, void* workspace, size_t workspace_bytes, void* stream,
                          void* const* step_events);
+
+/* Where moe_forward keeps its intermediate results inside the workspace, for
+ * a call with these arguments (the same rules moe_forward applies: the
+ * BLOCK_M of moe_get_block_m when block_m is 0, and K splits only when the
+ * workspace holds their float32 parts).  Offsets are bytes from the
+ * workspace's start, -1 for a buffer the format does not use.  After a
+ * forward the buffers hold (M = offsets[E'] padded rows, S slots):
+ *   counts, offsets, sorted_slot, slot_row, tile_expert   int32, as
+ *       moe_dispatch writes them
+ *   xq, xq_sf, x_tok   the dispatch-quantised x as moe_quantize_x writes it
+ *       (MX: E4M3 [T, H] + UE8M0 [T, H/32]; NVFP4: packed E2M1 [T, H/2] +
+ *       E4M3 [T, H/16] + float32 token scales [T]); -1 for BF16
+ *   a1_sf   xq_sf of each sorted row, one plane per K block: byte m of plane
+ *       b (at a1_sf + b * sf_plane) is block b's scale of sorted row m
+ *   a2, a2_sf   the L2 input of each sorted row: MX E4M3 [M, I] (row
+ *       stride a2_ld bytes) with UE8M0 planes per 32 columns; NVFP4 packed
+ *       E2M1 [M, I/2] with E4M3 planes per 16 columns (global scale
+ *       l2_activation_scale); BF16 stage-blocked [M / block_m][I / 32]
+ *       [block_m][32] BF16 values (a2_sf -1)
+ *   o       the L2 output by slot: BF16 [S, H] when l2_rows_bf16, else
+ *       float32, l2_ksplit parts of [S, H] one after another
+ * The layout is for inspection (tests, debugging); it is not a stable
+ * interface.  Returns MOE_OK, MOE_E_INVALID (the shape checks of
+ * moe_forward) or MOE_E_WORKSPACE.  Host-only. */
+typedef struct {
+  int block_m;
+  int l1_ksplit, l2_ksplit;
+  int l2_rows_bf16;
+  int64_t sf_plane, a2_ld;
+  int64_t counts, offsets, sorted_slot, slot_row, tile_expert;
+  int64_t xq, xq_sf, x_tok, a1_sf;
+  int64_t a2, a2_sf;
+  int64_t o;
+  int64_t bytes;
+} moe_workspace_layout_t;
+int moe_workspace_layout(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
+                         int num_local_experts, int num_shared, int block_m, size_t workspace_bytes,
+                         moe_workspace_layout_t* layout);
 
 #ifdef __cplusplus
 }

@@ -205,3 +205,39 @@ def moe_reference(fmt, x_bits, topk_ids, topk_weights, w, *, num_shared=0,
         o = a_hat @ W2.T                                       # [n, H]
         np.add.at(y, r, wts[r, j][:, None] * o)
     return y if norm is None else post_expert_norm(y, *norm)
+
+
+def slot_activations(fmt, x_bits, topk_ids, w, *, num_shared=0, expert_start=0, num_local=None, act=None,
+                     tokens=None):
+    """The values the L2-input quantiser receives: for every slot that
+    reaches a local expert, a = act(g, u) with [g; u] = Deq(W13_e) @ x_hat,
+    float64 (the steps of ``moe_reference`` up to the L2-input
+    quantisation).
+
+    Returns (slots, experts, a): flat slot ids t * k' + j (t the token's
+    index in ``x_bits``) [n], their local experts [n] and the activations
+    [n, I], ordered by expert, then by slot.  ``tokens``: restrict to these
+    token indices."""
+    act = dict(act or {})
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T = x_bits.shape[0]
+    E_all = w["w13"].shape[0]
+    if num_local is None:
+        num_local = E_all - num_shared
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xs = quantize_x(fmt, x_bits[tok])
+    exp = slot_experts(np.asarray(topk_ids)[tok], num_shared, expert_start, num_local)
+    kk = exp.shape[1]
+    slots, experts, acts = [], [], []
+    for e in np.unique(exp[exp >= 0]):
+        r, j = np.nonzero(exp == e)
+        W13 = dequant_weight(fmt, w, "w13", e)
+        I = W13.shape[0] // 2
+        h = xs[r] @ W13.T
+        acts.append(activation(h[:, :I], h[:, I:], act.get("clamp"), act.get("alpha", 1.0), act.get("beta", 0.0)))
+        slots.append(tok[r] * kk + j)
+        experts.append(np.full(r.size, e))
+    if not slots:
+        I = w["w2"].shape[-1] * (2 if fmt in ("mxfp4", "nvfp4") else 1)
+        return np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros((0, I))
+    return np.concatenate(slots), np.concatenate(experts), np.concatenate(acts)

@@ -52,6 +52,21 @@ def make_weights(cfg, fmt=None, seed=0, sources=None):
     return out
 
 
+# Parity figures of this session (GPU tests), printed one line per case at
+# the end of the run by tests/conftest.py.
+PARITY = []
+
+
+def record_parity(case, **stats):
+    PARITY.append((case, stats))
+
+
+def rescue_cap(n_tokens):
+    """Tokens the boundary-decision rule may accept in one comparison: half a
+    percent of them, and at least one."""
+    return max(1, int(0.005 * n_tokens))
+
+
 def bf16_half_ulp(y):
     """Half a unit in the last place of BF16 at |y| (the output container's
     own rounding)."""
@@ -78,6 +93,23 @@ def check_output(fmt, y_gpu, y_ref, rms=None):
     return float(err.max() / rms) if err.size and rms > 0 else 0.0, excess
 
 
+def error_summary(y_gpu, y_ref):
+    """The output error apart from the BF16 container's own rounding:
+    max(|y_gpu - y_ref| - half an ulp of y_ref) / RMS (the computation's
+    share, <= 0 when every output is within its own rounding), and the
+    largest distance from the round-to-nearest-even BF16 of the oracle, in
+    BF16 ulps of that value."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if not y_ref.size:
+        return {"excess_over_rounding_per_rms": 0.0, "max_ulps_from_rne": 0.0}
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) or 1.0
+    rne = codecs.bf16_round_f64(y_ref)
+    ulp = 2.0 * bf16_half_ulp(rne)
+    return {"excess_over_rounding_per_rms": float((np.abs(y_gpu - y_ref) - bf16_half_ulp(y_ref)).max() / rms),
+            "max_ulps_from_rne": float((np.abs(y_gpu - rne) / ulp).max())}
+
+
 # --------------------------------------------------------------------------
 # L2-input quantisation decisions that sit on a boundary
 # --------------------------------------------------------------------------
@@ -96,17 +128,124 @@ def check_output(fmt, y_gpu, y_ref, rms=None):
 # accumulation), carried through the activation, plus 2^-18 relative
 # (hardware exp and reciprocal).
 
-def _act_error(W13, xs, act):
-    """float64 activations a [I] of one slot and a bound on their float32
-    evaluation error."""
+def accumulation_bound(fmt, K):
+    """Bound, relative to the sum of |products|, on the float32 evaluation
+    error of one L1 output (K products): the GPU adds one MFMA K-step's
+    products (16 for BF16 and NVFP4, 64 for the scaled MX MFMA) into a
+    float32 accumulator at a time, at most one rounding (2^-24 relative) per
+    step, plus the K-split parts and NVFP4's two scale products; doubled for
+    margin."""
+    kstep = 64 if fmt in ("mxfp8", "mxfp4") else 16
+    return 2.0 * (K // kstep + 4) * 2.0 ** -24
+
+
+def _act_error_rows(fmt, W13, X, act):
+    """float64 activations a [n, I] of n slots of one expert (inputs X [n, H])
+    and a bound on their float32 evaluation error: the accumulation bound of
+    g and u carried through the activation, plus 2^-18 relative for the
+    hardware exp and reciprocal."""
     I = W13.shape[0] // 2
-    h = W13 @ xs
-    eh = np.ldexp(np.abs(W13) @ np.abs(xs), -19)
+    h = X @ W13.T
+    eh = (np.abs(X) @ np.abs(W13).T) * accumulation_bound(fmt, W13.shape[1])
     f = lambda g, u: activation(g, u, act.get("clamp"), act.get("alpha", 1.0), act.get("beta", 0.0))
-    g, u, eg, eu = h[:I], h[I:], eh[:I], eh[I:]
+    g, u, eg, eu = h[:, :I], h[:, I:], eh[:, :I], eh[:, I:]
     a = f(g, u)
     da = np.max([np.abs(f(g + sg * eg, u + su * eu) - a) for sg in (-1, 1) for su in (-1, 1)], axis=0)
     return a, da + np.ldexp(np.abs(a), -18)
+
+
+def _act_error(W13, xs, act, fmt="mxfp8"):
+    """_act_error_rows for one slot."""
+    a, da = _act_error_rows(fmt, W13, xs[None, :], act)
+    return a[0], da[0]
+
+
+def slot_l2_inputs(fmt, x_bits, ids, w, *, num_shared=0, expert_start=0, num_local=None, act=None, tokens=None):
+    """(slots, experts, a, da): the oracle's activations of every live slot
+    (oracle.moe.slot_activations) and a bound on the float32 evaluation
+    error with which the GPU computes them."""
+    from oracle.moe import slot_activations
+    act = dict(act or {})
+    slots, experts, a = slot_activations(fmt, x_bits, ids, w, num_shared=num_shared, expert_start=expert_start,
+                                         num_local=num_local, act=act, tokens=tokens)
+    kk = np.asarray(ids).shape[1] + num_shared
+    da = np.zeros_like(a)
+    for e in np.unique(experts):
+        sel = np.nonzero(experts == e)[0]
+        X = quantize_x(fmt, np.asarray(x_bits)[slots[sel] // kk])
+        _, da[sel] = _act_error_rows(fmt, dequant_weight(fmt, w, "w13", e), X, act)
+    return slots, experts, a, da
+
+
+def _allowed(dec, enc, v, dv, got):
+    """Element codes ``got`` that some value in [v - dv, v + dv] encodes to:
+    the decoded value lies between those of the interval's ends (encoding
+    is monotone), and a zero's sign bit is one of the interval's signs."""
+    lo, hi = enc(v - dv), enc(v + dv)
+    gv, lv, hv = dec(got), dec(lo), dec(hi)
+    ok = (gv >= np.minimum(lv, hv)) & (gv <= np.maximum(lv, hv))
+    sign_bit = 0x8000 if got.dtype == np.uint16 else (0x8 if dec is codecs.e2m1_decode else 0x80)
+    neg = (got & sign_bit) != 0
+    zero = gv == 0
+    ok &= ~zero | np.where(neg, v - dv <= 0, v + dv >= 0)
+    return ok
+
+
+def l2_code_check(fmt, codes, scales, a, da, g2=1.0):
+    """The GPU's L2-input codes of n slots (``codes`` [n, I]: BF16 bits, or
+    unpacked E4M3 / E2M1 codes; ``scales`` [n, I/32] UE8M0 or [n, I/16]
+    E4M3) against the oracle's quantiser applied to the oracle's float32
+    activations ``a`` (evaluation error bound ``da``).  A code or block scale
+    may differ from the oracle's only where the activation lies within its
+    error bound of a decision boundary, i.e. where some value within the
+    bound is quantised to the GPU's decision.  Returns counts: elements,
+    element flips (codes unlike the oracle's, all of them boundary cases),
+    blocks, scale flips, and ``unexplained`` (differences not so covered;
+    must be 0)."""
+    a = np.asarray(a, dtype=np.float64)
+    da = np.asarray(da, dtype=np.float64)
+    n, I = a.shape
+    a32 = a.astype(np.float32)
+    if fmt == "bf16":
+        own = codecs.bf16_encode_f32(a32)
+        f32 = lambda v: codecs.bf16_encode_f32(np.asarray(v).astype(np.float32))
+        ok = _allowed(codecs.bf16_decode, f32, a, da, codes)
+        return {"elements": int(a.size), "element_flips": int((codes != own).sum()), "blocks": 0,
+                "scale_flips": 0, "unexplained": int((~ok).sum())}
+    grp = 16 if fmt == "nvfp4" else 32
+    nb = I // grp
+    blk = a.reshape(n, nb, grp)
+    dblk = da.reshape(n, nb, grp)
+    got_c = np.asarray(codes).reshape(n, nb, grp)
+    got_s = np.asarray(scales).reshape(n, nb)
+    amax_lo = np.maximum(np.abs(blk) - dblk, 0.0).max(-1)
+    amax_hi = (np.abs(blk) + dblk).max(-1)
+    if fmt in ("mxfp8", "mxfp4"):
+        own_q, own_s = quant.mx_quantize(a32, "e4m3")
+        s_lo = quant.mx_scale_codes(amax_lo.astype(np.float32), "e4m3")
+        s_hi = quant.mx_scale_codes(amax_hi.astype(np.float32), "e4m3")
+        scale_ok = (got_s >= s_lo) & (got_s <= s_hi)
+        # elements under the GPU's own block scale
+        mul = np.where(got_s > 0, np.ldexp(1.0, 127 - got_s.astype(np.int64)), 0.0)[..., None]
+        ok = _allowed(codecs.e4m3_decode, codecs.e4m3_encode, blk * mul, dblk * mul, got_c)
+        ok |= (got_s == 0)[..., None] & (got_c == 0)
+    else:
+        g = np.float32(g2)
+        own_q, own_s = quant.nvfp4_quantize(a32, np.full(n, g, dtype=np.float32))
+        six_g = np.float32(np.float32(6.0) * g)
+        s_lo = codecs.e4m3_encode((amax_lo / float(six_g)).astype(np.float32))
+        s_hi = codecs.e4m3_encode((amax_hi / float(six_g)).astype(np.float32))
+        sv = codecs.e4m3_decode(got_s)
+        scale_ok = (sv >= codecs.e4m3_decode(s_lo)) & (sv <= codecs.e4m3_decode(s_hi)) & (got_s < 0x80)
+        r = np.where(sv > 0, (np.float32(1.0) / np.maximum(sv * g, 1e-30).astype(np.float32)).astype(np.float64),
+                     0.0)[..., None]
+        ok = _allowed(codecs.e2m1_decode, codecs.e2m1_encode, blk * r, dblk * r, got_c)
+        ok |= (sv == 0)[..., None] & ((got_c & 0x7) == 0)
+    own_q = own_q.reshape(n, nb, grp)
+    same_scale = got_s == own_s
+    return {"elements": int(a.size), "element_flips": int(((got_c != own_q) & same_scale[..., None]).sum()),
+            "blocks": int(got_s.size), "scale_flips": int((~same_scale).sum()),
+            "unexplained": int((~ok).sum() + (~scale_ok).sum())}
 
 
 def decision_alternatives(fmt, a, da, g2=1.0):
@@ -177,7 +316,7 @@ def decision_alternatives(fmt, a, da, g2=1.0):
 
 
 def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_start=0, num_local=None,
-                act=None, g2=1.0, tokens=None, max_decisions=12, norm=None, y_pre=None):
+                act=None, g2=1.0, tokens=None, max_decisions=12, norm=None, y_pre=None, name=None):
     """check_output, plus the boundary-decision rule above for tokens over
     the bar (every combination of a token's boundary decisions when there are
     at most ``max_decisions``, else a greedy search).  ``tokens``: the token
@@ -187,8 +326,15 @@ def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_
     y_ref = np.asarray(y_ref, dtype=np.float64)
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
     rel, excess = check_output(fmt, y_gpu, y_ref, rms=rms)
+
+    def done(worst, rescued):
+        if name is not None:
+            record_parity(name, tokens=int(y_ref.shape[0]), max_err_per_rms=rel, worst_excess=worst,
+                          rescued=rescued, rescue_cap=rescue_cap(y_ref.shape[0]), **error_summary(y_gpu, y_ref))
+        return rel, worst, rescued
+
     if excess <= 0 or fmt == "bf16":
-        return rel, excess, 0
+        return done(excess, 0)
 
     def row_excess(yg, yr):
         return float((np.abs(yg - yr) - (TOL[fmt] * rms + bf16_half_ulp(yr))).max())
@@ -223,7 +369,7 @@ def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_
             if e not in cache:
                 cache[e] = (dequant_weight(fmt, w, "w13", e), dequant_weight(fmt, w, "w2", e))
             W13, W2 = cache[e]
-            a, da = _act_error(W13, xs, act)
+            a, da = _act_error(W13, xs, act, fmt)
             wj = float(wts[t, j]) if j < k else 1.0
             for off, dv in decision_alternatives(fmt, a, da, g2):
                 deltas.append(wj * (W2[:, off:off + dv.size] @ dv))
@@ -251,4 +397,4 @@ def check_layer(fmt, y_gpu, y_ref, x_bits, ids, wts, w, *, num_shared=0, expert_
         if best <= 0:
             rescued += 1
         worst = max(worst, best)
-    return rel, worst, rescued
+    return done(worst, rescued)

@@ -24,7 +24,8 @@ def _setup(fmt, monkeypatch, widen=2.0 ** 4):
     # widen the evaluation-error bound so that some decisions count as boundary
     # decisions in this small case
     real = helpers._act_error
-    monkeypatch.setattr(helpers, "_act_error", lambda W13, xs, act: (lambda a, da: (a, da * widen))(*real(W13, xs, act)))
+    monkeypatch.setattr(helpers, "_act_error",
+                        lambda W13, xs, act, fmt="mxfp8": (lambda a, da: (a, da * widen))(*real(W13, xs, act, fmt)))
     return cfg, x, ids, wts, w, g2, ref
 
 

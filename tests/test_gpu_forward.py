@@ -14,8 +14,8 @@ import torch
 
 from oracle.moe import moe_reference
 from synth import CONFIGS, MoEConfig, gen_routing, gen_x_bf16, gen_w2_input_scale, bf16_bits
-from tests.gpu_util import run_layer
-from tests.helpers import check_layer, check_output, make_weights
+from tests.gpu_util import dev, run_layer, x_dev
+from tests.helpers import check_layer, check_output, make_weights, rescue_cap
 
 pytestmark = pytest.mark.gpu
 
@@ -54,25 +54,27 @@ def inputs(cfg):
     return _CACHE[cfg.name]
 
 
-def l2_scale(cfg):
-    """NVFP4: the experts' w2 input scales and their max (1.0 if 0), the one
-    global scale every L2 input is quantised with."""
+def l2_scale(cfg, factor=1.0):
+    """NVFP4: the experts' w2 input scales (times ``factor``) and their max
+    (1.0 if 0), the one global scale every L2 input is quantised with."""
     if cfg.fmt != "nvfp4":
         return None, 1.0
-    w2in = gen_w2_input_scale(cfg)
+    w2in = (gen_w2_input_scale(cfg) * np.float32(factor)).astype(np.float32)
     m = float(w2in.max())
     return w2in, (m if m > 0 else 1.0)
 
 
-def compare(cfg, block_m=0, act=None, **kw):
+def compare(cfg, block_m=0, act=None, w2in_scale=1.0, tag="", **kw):
     x, ids, wts, w = inputs(cfg)
-    w2in, g2 = l2_scale(cfg)
+    w2in, g2 = l2_scale(cfg, w2in_scale)
     y, _ = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, block_m=block_m, act=act,
                      w2_input_scale=w2in, **kw)
     ref = moe_reference(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, act=act, l2_activation_scale=g2)
-    rel, excess, alt = check_layer(cfg.fmt, y, ref, x, ids, wts, w, num_shared=cfg.num_shared, act=act, g2=g2)
+    rel, excess, alt = check_layer(cfg.fmt, y, ref, x, ids, wts, w, num_shared=cfg.num_shared, act=act, g2=g2,
+                                   name=f"{cfg.name} bm={block_m}{tag}")
     print(f"{cfg.name} bm={block_m}: max|err|/RMS = {rel:.3e}, tokens under another valid L2-input decision: {alt}")
     assert excess <= 0, (rel, excess)
+    assert alt <= rescue_cap(cfg.T), alt
     return y
 
 
@@ -107,10 +109,54 @@ def test_forward_independent_of_block_m(name):
         assert np.array_equal(ys[0], y), bm
 
 
-def test_forward_activation_variants():
-    cfg = SMALL["bf16_small"]
-    compare(cfg, act={"clamp": 0.75, "alpha": 1.702, "beta": 1.0})
-    compare(cfg, act={"clamp": None, "alpha": 0.5, "beta": -0.25})
+ACT_VARIANTS = [{"clamp": 0.75, "alpha": 1.702, "beta": 1.0}, {"clamp": None, "alpha": 0.5, "beta": -0.25},
+                {"clamp": 0.0, "alpha": 1.0, "beta": 0.0}]
+
+
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small", "bf16_decode",
+                                  "mxfp8_decode", "mxfp4_decode", "nvfp4_decode"])
+def test_forward_activation_variants(name):
+    """MegaMoEActivation's clamp, alpha and beta in every format's L1
+    epilogue, and in the finish kernel of a K-split L1 (decode-sized
+    launches)."""
+    cfg = {**SMALL, **DECODE_SMALL}[name]
+    for i, act in enumerate(ACT_VARIANTS):
+        compare(cfg, act=act, tag=f" act{i}")
+
+
+@pytest.mark.parametrize("name", ["nvfp4_small", "nvfp4_decode"])
+def test_forward_nvfp4_saturated_l2_input(name):
+    """An NVFP4 L2 input scale 64 times below the calibrated one: many L2
+    input block scales clamp at 448 and elements at 6, in the L1 epilogue and
+    in the K-split finish kernel; the oracle applies the same scale."""
+    compare({**SMALL, **DECODE_SMALL}[name], w2in_scale=1.0 / 64, tag=" saturated")
+
+
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small", "mxfp4_decode"])
+def test_forward_writes_nothing_outside_out_and_workspace(name):
+    """Guard bands of a known pattern around ``out`` and the workspace are
+    untouched by a forward, and every element of ``out`` is written."""
+    from expert_gemms_amd import _lib
+    cfg = {**SMALL, **DECODE_SMALL}[name]
+    x, ids, wts, w = inputs(cfg)
+    w2in, _ = l2_scale(cfg)
+    _, layer = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
+    G = 1 << 16                                          # guard bytes on each side
+    n_out = cfg.T * cfg.H * 2
+    out_buf = torch.full((G + n_out + G,), 0x5A, dtype=torch.uint8, device="cuda")
+    out_buf[G:G + n_out] = 0xFF                          # BF16 NaNs until written
+    out = out_buf[G:G + n_out].view(torch.bfloat16).view(cfg.T, cfg.H)
+    nws = layer.workspace.numel()
+    ws_buf = torch.full((G + nws + G,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = ws_buf[G:G + nws]
+    _lib.moe_forward(cfg.fmt, cfg.T, cfg.H, cfg.I, cfg.top_k, 0, cfg.E, cfg.num_shared, 0, None, x_dev(x),
+                     dev(ids.astype(np.int32)), dev(wts.astype(np.float32)), layer.w13_k, layer.w13_sf_k,
+                     layer.w2_k, layer.w2_sf_k, layer.w13_gs, layer.w2_gs, layer.l2_activation_scale, out, ws)
+    torch.cuda.synchronize()
+    ob, wb = out_buf.cpu().numpy(), ws_buf.cpu().numpy()
+    assert (ob[:G] == 0x5A).all() and (ob[G + n_out:] == 0x5A).all()
+    assert (wb[:G] == 0xA5).all() and (wb[G + nws:] == 0xA5).all()
+    assert torch.isfinite(out.float()).all()
 
 
 def test_forward_expert_range_and_dropped_slots():

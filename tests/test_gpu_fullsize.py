@@ -1,19 +1,27 @@
 """The HIP layer at the full sizes of the five seeded workloads, in the launch
-configuration bench.py times (default BLOCK_M), against the oracle on
-sampled tokens.
+configuration bench.py times (the library's BLOCK_M and K-split rules),
+against the oracle over whole outputs.
 
-Full-size weight sets are drawn on the device (synth.gen_weight_f32_device)
-and, for the MX/NVFP4 formats, quantised by the library.  For the sampled
-tokens' experts the oracle re-quantises the same float32 draws with its own
-quantiser (in a process pool) and the GPU's codes must match them bit for
-bit; the oracle then computes those tokens' outputs from its own codes.
-Routing metadata is checked bit-exact at full size.  Bar: as in
-tests/helpers.check_layer, with RMS taken over the sampled outputs.
+Weights: each expert's float32 draws (synth.gen_weight_f32) are quantised by
+the oracle's quantisers (tests/helpers.quantize_weight) in a process pool;
+the same canonical arrays go to the GPU (moe_transform_weights) and to the
+oracle, so no oracle input comes from the HIP path.
+
+Compared: every token of the Mixtral-shaped BF16 layer, the NVFP4 Zipf layer
+and every decode batch, and 256 tokens of the DeepSeek-V3-shaped layer
+(nearly every one of its 257 experts); the oracle's output is the sum of
+per-expert-group contributions computed in the pool (the layer is a sum over
+slots; the shared expert enters as an always-present id of weight 1).  Also
+checked from the forward's own workspace: the routing metadata and the
+dispatch-quantised x bit-exact at full size, and the L2-input codes of the
+first 64 compared tokens against the oracle's quantiser.
 """
 
 import concurrent.futures
+import multiprocessing
 import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -23,38 +31,43 @@ import expert_gemms_amd as moe
 from oracle import codecs, quant
 from oracle.dispatch import dispatch_reference
 from oracle.moe import moe_reference
-from synth import CONFIGS, gen_routing, gen_w2_input_scale, gen_weight_f32_device, gen_x_bf16, bf16_bits
+from synth import CONFIGS, gen_routing, gen_w2_input_scale, gen_weight_f32, gen_x_bf16, bf16_bits
 from synth.configs import DECODE_TOKENS
-from tests.gpu_util import dev
-from tests.helpers import check_layer
+from tests.gpu_util import WorkspaceReader, dev
+from tests.helpers import (check_layer, l2_code_check, quantize_weight, record_parity, rescue_cap,
+                           slot_l2_inputs)
 
 pytestmark = pytest.mark.gpu
 
 CASES = [("tiny_bf16", None), ("mixtral_bf16", None), ("dsv3_mxfp8", None), ("nvfp4_zipf", None)] + \
         [("decode_mxfp4", t) for t in DECODE_TOKENS]
+COMPARED_TOKENS = {"dsv3_mxfp8": 256}
+L2_CHECK_TOKENS = 64
+WORKERS = min(16, os.cpu_count() or 1)
 
 
 def log(msg):
-    print(msg, flush=True)
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
     sys.stdout.flush()
 
 
-def _oracle_quantize(args):
-    """(fmt, float32 [N, K]) -> canonical arrays of one expert (oracle side)."""
-    fmt, w32 = args
-    if fmt == "mxfp8":
-        q, c = quant.mx_quantize(w32, "e4m3")
-        return {"w": q, "sf": c}
-    if fmt == "mxfp4":
-        q, c = quant.mx_quantize(w32, "e2m1")
-        return {"w": codecs.fp4_pack(q), "sf": c}
-    g = quant.nvfp4_global_scale(np.array(np.abs(w32).max(), dtype=np.float32))
-    q, bs = quant.nvfp4_quantize(w32, np.full(w32.shape[0], g, dtype=np.float32))
-    return {"w": codecs.fp4_pack(q), "sf": bs, "gs": np.float32(g)}
+def _limit_blas():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(2)
+    except Exception:
+        pass
+
+
+def _expert_weights(args):
+    """(workload, expert) -> canonical arrays of that expert (oracle side)."""
+    name, e = args
+    cfg = CONFIGS[name]
+    return e, {nm: quantize_weight(cfg.fmt, gen_weight_f32(cfg, nm, e)) for nm in ("w13", "w2")}
 
 
 class ExpertArray:
-    """Per-expert canonical arrays for the experts the oracle needs."""
+    """Per-expert canonical arrays indexed like the stacked [E', ...] array."""
     def __init__(self, n_experts, items):
         self.items = items
         self.shape = (n_experts,)
@@ -63,130 +76,192 @@ class ExpertArray:
         return self.items[int(e)]
 
 
-def pick_tokens(ids, n_tok, E):
-    """A few tokens (first one fixed) chosen greedily to share experts, so the
-    oracle re-quantises as few experts as possible."""
-    T = ids.shape[0]
-    chosen = [0]
-    experts = set(int(e) for e in ids[0] if 0 <= e < E)
-    rng = np.random.default_rng(123)
-    cand = rng.permutation(T)[:4096]
-    while len(chosen) < min(n_tok, T):
-        best, best_new = None, None
-        for t in cand:
-            if t in chosen:
-                continue
-            new = len(set(int(e) for e in ids[t] if 0 <= e < E) - experts)
-            if best_new is None or new < best_new:
-                best, best_new = int(t), new
-        chosen.append(best)
-        experts |= set(int(e) for e in ids[best] if 0 <= e < E)
-    chosen.append(T - 1)
-    return sorted(set(chosen))
+def _as_w(fmt, n_experts, per_expert):
+    w = {}
+    for nm in ("w13", "w2"):
+        w[nm] = ExpertArray(n_experts, {e: d[nm]["w"] for e, d in per_expert.items()})
+        if fmt != "bf16":
+            w[nm + "_sf"] = ExpertArray(n_experts, {e: d[nm]["sf"] for e, d in per_expert.items()})
+        if fmt == "nvfp4":
+            gs = np.zeros(n_experts, dtype=np.float32)
+            for e, d in per_expert.items():
+                gs[e] = d[nm]["gs"]
+            w[nm + "_gs"] = gs
+    return w
+
+
+def _oracle_part(args):
+    """The oracle's contribution of one group of experts to the compared
+    tokens, and (for the first tokens) the activations entering the L2-input
+    quantiser with their error bounds.  The canonical arrays come from the
+    parent's memory (a forked worker)."""
+    name, group, x_bits, ids_aug, wts_aug, g2, l2_tokens = args
+    cfg = CONFIGS[name]
+    fmt, n_experts = cfg.fmt, cfg.E + cfg.num_shared
+    per_expert = {e: _WEIGHTS[name][e] for e in group}
+    w = _as_w(fmt, n_experts, per_expert)
+    mine = np.isin(ids_aug, list(per_expert))
+    ids_m = np.where(mine, ids_aug, -1)
+    y = moe_reference(fmt, x_bits, ids_m, wts_aug, w, num_shared=0, num_local=n_experts,
+                      l2_activation_scale=g2)
+    l2 = slot_l2_inputs(fmt, x_bits[:l2_tokens], ids_m[:l2_tokens], w, num_shared=0, num_local=n_experts)
+    return y, l2
+
+
+_WEIGHTS = {}
+
+
+def oracle_weights(name, pool):
+    """Canonical arrays of every expert of a workload (cached: the decode
+    batches share one weight set)."""
+    if name not in _WEIGHTS:
+        cfg = CONFIGS[name]
+        E_all = cfg.E + cfg.num_shared
+        _WEIGHTS.clear()
+        _WEIGHTS[name] = dict(pool.map(_expert_weights, [(name, e) for e in range(E_all)]))
+    return _WEIGHTS[name]
+
+
+def upload(fmt, per_expert, E_all):
+    """Stacked canonical device tensors."""
+    out = {}
+    for nm in ("w13", "w2"):
+        out[nm] = dev(np.stack([per_expert[e][nm]["w"] for e in range(E_all)]))
+        if fmt != "bf16":
+            out[nm + "_sf"] = dev(np.stack([per_expert[e][nm]["sf"] for e in range(E_all)]))
+        if fmt == "nvfp4":
+            out[nm + "_gs"] = dev(np.array([per_expert[e][nm]["gs"] for e in range(E_all)], dtype=np.float32))
+    return out
+
+
+def compared_tokens(name, ids, T, E):
+    """All tokens, or for the largest layer a set chosen greedily to reach
+    as many (expert, first-seen) pairs as possible: each next token adds the
+    most experts not yet covered."""
+    n = COMPARED_TOKENS.get(name)
+    if n is None or n >= T:
+        return np.arange(T)
+    rng = np.random.default_rng(321)
+    cand = rng.permutation(T)[:4 * n]
+    chosen, seen = [], set()
+    left = list(cand)
+    while len(chosen) < n:
+        gains = [len(set(int(e) for e in ids[t] if 0 <= e < E) - seen) for t in left]
+        i = int(np.argmax(gains))
+        t = left.pop(i)
+        chosen.append(int(t))
+        seen |= set(int(e) for e in ids[t] if 0 <= e < E)
+    return np.array(sorted(chosen))
+
+
+def expert_groups(counts, n_groups):
+    """Experts split into groups of about equal slot counts (largest first)."""
+    order = np.argsort(-counts, kind="stable")
+    groups = [[] for _ in range(n_groups)]
+    load = np.zeros(n_groups)
+    for e in order:
+        if counts[e] == 0:
+            continue
+        g = int(np.argmin(load))
+        groups[g].append(int(e))
+        load[g] += counts[e] + 1
+    return [g for g in groups if g]
 
 
 @pytest.mark.parametrize("name,tokens", CASES, ids=[f"{n}-{t}" if t else n for n, t in CASES])
-def test_fullsize_sampled(name, tokens):
+def test_fullsize(name, tokens):
     cfg = CONFIGS[name]
     T = tokens if tokens is not None else cfg.T
     fmt, H, I = cfg.fmt, cfg.H, cfg.I
     E_all = cfg.E + cfg.num_shared
-    log(f"[fullsize] {name} T={T} fmt={fmt}: inputs")
+    kk = cfg.top_k + cfg.num_shared
+    log(f"{name} T={T} fmt={fmt}: inputs")
     x = gen_x_bf16(cfg, T)
+    xb = bf16_bits(x)
     ids, wts = gen_routing(cfg, T)
-    bm = moe.moe_get_block_m(T, cfg.E, cfg.num_shared, cfg.top_k, fmt)
+    fork = multiprocessing.get_context("fork")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=WORKERS, initializer=_limit_blas,
+                                                mp_context=fork) as pool:
+        per_expert = oracle_weights(name, pool)
+    log(f"{name}: {E_all} experts quantised by the oracle's quantisers")
+    # a pool forked now sees the canonical arrays without copying them over
+    with concurrent.futures.ProcessPoolExecutor(max_workers=WORKERS, initializer=_limit_blas,
+                                                mp_context=fork) as pool:
 
-    # routing metadata at full size, bit-exact
-    S = T * (cfg.top_k + cfg.num_shared)
-    M = S + E_all * (bm - 1)
-    d = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
-    cnt, off, ss, sr, te = d(E_all), d(E_all + 1), d(M), d(S), d(M // bm + 1)
-    ids_d = dev(ids)
-    # with the scratch moe_forward's workspace provides (many workgroups from
-    # 16384 slots on, as in the forward)
-    bc = d(moe._lib.dispatch_scratch_ints(T, cfg.top_k, cfg.num_shared, cfg.E))
-    moe.moe_dispatch(T, cfg.top_k, cfg.num_shared, 0, cfg.E, bm, ids_d, cnt, off, ss, sr, te, block_counts=bc)
-    ref_d = dispatch_reference(ids, cfg.num_shared, 0, cfg.E, bm)
-    Mp = int(ref_d["offsets"][-1])
-    got = {"counts": cnt.cpu().numpy()[:E_all], "offsets": off.cpu().numpy(), "sorted_slot": ss.cpu().numpy()[:Mp],
-           "slot_row": sr.cpu().numpy()[:S], "tile_expert": te.cpu().numpy()[:Mp // bm]}
-    for k in ref_d:
-        assert np.array_equal(got[k], ref_d[k]), k
-    log(f"[fullsize] {name}: dispatch bit-exact (BLOCK_M {bm}, {Mp} padded rows)")
+        # the GPU forward, default BLOCK_M and K splits
+        canon = upload(fmt, per_expert, E_all)
+        layer = moe.FusedMoE(fmt, H, I, cfg.E, cfg.top_k, num_shared=cfg.num_shared, max_tokens=T)
+        w2in = gen_w2_input_scale(cfg) if fmt == "nvfp4" else None
+        layer.load_canonical(canon["w13"], canon["w2"], canon.get("w13_sf"), canon.get("w2_sf"),
+                             canon.get("w13_gs"), canon.get("w2_gs"),
+                             w2_input_scale=None if w2in is None else torch.from_numpy(w2in))
+        y = layer.forward(x.cuda(), dev(ids), dev(wts))
+        torch.cuda.synchronize()
+        y = y.float().cpu().numpy().astype(np.float64)
+        del canon
+        ws = WorkspaceReader(layer, T)
+        log(f"{name}: GPU forward done (BLOCK_M {ws.bm}, L1 split {ws.lay['l1_ksplit']}, "
+            f"L2 split {ws.lay['l2_ksplit']})")
 
-    sample = pick_tokens(ids, 3 if fmt != "bf16" else 6, cfg.E)
-    needed = sorted(set(int(e) for t in sample for e in ids[t] if 0 <= e < cfg.E) |
-                    set(range(cfg.E, E_all)))
-    log(f"[fullsize] {name}: sampled tokens {sample}, {len(needed)} experts for the oracle")
-
-    # weights: drawn on the device, quantised by the library
-    vpe = 2 if fmt in ("mxfp4", "nvfp4") else 1
-    grp = 16 if fmt == "nvfp4" else 32
-    canon, host32 = {}, {"w13": {}, "w2": {}}
-    for nm, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
-        if fmt == "bf16":
-            wt = torch.empty((E_all, N, K), dtype=torch.bfloat16, device="cuda")
-        else:
-            wt = torch.empty((E_all, N, K // vpe), dtype=torch.uint8, device="cuda")
-            sf = torch.empty((E_all, N, K // grp), dtype=torch.uint8, device="cuda")
-            gs = torch.empty((E_all,), dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
-        for e in range(E_all):
-            src = gen_weight_f32_device(cfg, nm, e, "cuda")
-            if e in needed:
-                host32[nm][e] = src.cpu().numpy()
-            if fmt == "bf16":
-                wt[e].copy_(src)
-            else:
-                moe.moe_quantize_weights(fmt, 1, N, K, src, wt[e], sf[e], gs[e:e + 1] if gs is not None else None)
-        canon[nm] = wt
+        # routing metadata and dispatch-quantised x of the forward, bit-exact
+        ref_d = dispatch_reference(ids, cfg.num_shared, 0, cfg.E, ws.bm)
+        got = ws.dispatch()
+        for k in ref_d:
+            assert np.array_equal(got[k], ref_d[k]), k
         if fmt != "bf16":
-            canon[nm + "_sf"] = sf
-            if gs is not None:
-                canon[nm + "_gs"] = gs
-    torch.cuda.synchronize()
-    log(f"[fullsize] {name}: weights ready")
+            x32 = codecs.bf16_decode(xb).astype(np.float32)
+            codes, scales, tok = ws.xq()
+            if fmt == "nvfp4":
+                g = quant.nvfp4_global_scale(np.abs(x32).max(axis=1))
+                q, bs = quant.nvfp4_quantize(x32, g)
+                assert np.array_equal(tok, g)
+            else:
+                q, bs = quant.mx_quantize(x32, "e4m3")
+            assert np.array_equal(codes, q) and np.array_equal(scales, bs)
+        log(f"{name}: dispatch and dispatch quantisation bit-exact ({int(ref_d['offsets'][-1])} padded rows)")
 
-    layer = moe.FusedMoE(fmt, H, I, cfg.E, cfg.top_k, num_shared=cfg.num_shared, max_tokens=T)
-    w2in = gen_w2_input_scale(cfg) if fmt == "nvfp4" else None
-    layer.load_canonical(canon["w13"], canon["w2"], canon.get("w13_sf"), canon.get("w2_sf"),
-                         canon.get("w13_gs"), canon.get("w2_gs"),
-                         w2_input_scale=None if w2in is None else torch.from_numpy(w2in))
-    y = layer.forward(x.cuda(), ids_d, dev(wts))
-    torch.cuda.synchronize()
-    y = y.float().cpu().numpy().astype(np.float64)
-    log(f"[fullsize] {name}: GPU forward done")
+        # the oracle over the compared tokens, by groups of experts
+        sample = compared_tokens(name, ids, T, cfg.E)
+        ids_aug = np.concatenate([ids[sample].astype(np.int64),
+                                  np.broadcast_to(cfg.E + np.arange(cfg.num_shared), (sample.size, cfg.num_shared))],
+                                 axis=1)
+        wts_aug = np.concatenate([wts[sample].astype(np.float64), np.ones((sample.size, cfg.num_shared))], axis=1)
+        counts = np.bincount(ids_aug[ids_aug >= 0].ravel(), minlength=E_all)
+        groups = expert_groups(counts, min(WORKERS * 2, E_all))
+        g2 = 1.0
+        if fmt == "nvfp4":
+            m = float(w2in.max())
+            g2 = m if m > 0 else 1.0
+        l2_tokens = min(L2_CHECK_TOKENS, sample.size)
+        jobs = [(name, grp, xb[sample], ids_aug, wts_aug, g2, l2_tokens) for grp in groups]
+        ref = np.zeros((sample.size, H))
+        l2_parts = []
+        for part, l2 in pool.map(_oracle_part, jobs):
+            ref += part
+            l2_parts.append(l2)
+    log(f"{name}: oracle done on {sample.size} tokens over {len(groups)} expert groups")
 
-    # oracle-side canonical arrays of the needed experts, checked against the GPU's
-    w = {}
-    if fmt == "bf16":
-        for nm in ("w13", "w2"):
-            items = {e: bf16_bits(torch.from_numpy(host32[nm][e]).to(torch.bfloat16)) for e in needed}
-            w[nm] = ExpertArray(E_all, items)
-    else:
-        with concurrent.futures.ProcessPoolExecutor(max_workers=8) as ex:
-            for nm in ("w13", "w2"):
-                res = dict(zip(needed, ex.map(_oracle_quantize, [(fmt, host32[nm][e]) for e in needed])))
-                for e in needed:
-                    assert np.array_equal(canon[nm][e].cpu().numpy(), res[e]["w"]), (nm, e)
-                    assert np.array_equal(canon[nm + "_sf"][e].cpu().numpy(), res[e]["sf"]), (nm, e)
-                    if fmt == "nvfp4":
-                        assert canon[nm + "_gs"][e].item() == res[e]["gs"], (nm, e)
-                w[nm] = ExpertArray(E_all, {e: res[e]["w"] for e in needed})
-                w[nm + "_sf"] = ExpertArray(E_all, {e: res[e]["sf"] for e in needed})
-                if fmt == "nvfp4":
-                    gsv = np.zeros(E_all, dtype=np.float32)
-                    for e in needed:
-                        gsv[e] = res[e]["gs"]
-                    w[nm + "_gs"] = gsv
-        log(f"[fullsize] {name}: GPU weight codes equal the oracle's for {len(needed)} experts")
-    g2 = 1.0
-    if fmt == "nvfp4":
-        m = float(w2in.max())
-        g2 = m if m > 0 else 1.0
-    ref = moe_reference(fmt, bf16_bits(x), ids, wts, w, num_shared=cfg.num_shared, tokens=sample,
-                        l2_activation_scale=g2)
-    rel, excess, alt = check_layer(fmt, y[sample], ref, bf16_bits(x), ids, wts, w, num_shared=cfg.num_shared,
-                                   g2=g2, tokens=sample)
-    log(f"[fullsize] {name}: sampled max|err|/RMS = {rel:.3e}; tokens under another valid L2-input decision: {alt}")
+    # the layer output
+    w = _as_w(fmt, E_all, per_expert)
+    rel, excess, alt = check_layer(fmt, y[sample], ref, xb[sample], ids_aug, wts_aug, w, num_shared=0,
+                                   num_local=E_all, g2=g2, name=f"fullsize {name} T={T}")
+    log(f"{name}: max|err|/RMS = {rel:.3e} over {sample.size} tokens; "
+        f"tokens under another valid L2-input decision: {alt}")
     assert excess <= 0, (rel, excess)
+    assert alt <= rescue_cap(sample.size), alt
     assert np.isfinite(y).all()
+
+    # L2-input codes of the first compared tokens (slot ids of the augmented
+    # routing map back to the forward's slots: same token order, k' columns)
+    slots = np.concatenate([p[0] for p in l2_parts])
+    a = np.concatenate([p[2] for p in l2_parts])
+    da = np.concatenate([p[3] for p in l2_parts])
+    fwd_slots = sample[slots // kk] * kk + slots % kk
+    rows = got["slot_row"][fwd_slots]
+    assert (rows >= 0).all()
+    codes, scales = ws.l2_input(rows)
+    st = l2_code_check(fmt, codes, scales, a, da, g2=g2)
+    record_parity(f"fullsize L2 input {name} T={T} ({l2_tokens} tokens)", **st)
+    log(f"{name}: L2-input codes {st}")
+    assert st["unexplained"] == 0, st
+    assert st["element_flips"] <= max(2, 1e-3 * st["elements"]), st

@@ -238,3 +238,33 @@ def test_activation_variants_closed_forms():
     c = 1.5
     ref = np.minimum(g, c) / (1 + np.exp(-1.702 * np.minimum(g, c))) * (np.clip(u, -c, c) + 1.0)
     assert np.allclose(M.activation(g, u, clamp=c, alpha=1.702, beta=1.0), ref, rtol=1e-14)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_slot_activations_equal_the_dense_route(fmt):
+    """slot_activations (the values entering the L2-input quantiser) equal
+    silu(G) * U of the dense torch route, picked at each slot's expert, for
+    every slot of a top-2 routing with a shared expert."""
+    cfg = small_cfg(fmt, T=20, E=5, k=2, n_sh=1, cid=97)
+    x = bf16_bits(gen_x_bf16(cfg))
+    ids, _ = gen_routing(cfg)
+    ids = ids.copy()
+    ids[3, 1] = -1                                              # a dropped slot has no activation
+    w = make_weights(cfg)
+    slots, experts, a = M.slot_activations(fmt, x, ids, w, num_shared=1)
+    X = torch_x(fmt, x)
+    W13 = torch_dequant(fmt, w, "w13")
+    I = W13.shape[1] // 2
+    G = torch.einsum("th,eih->tei", X, W13[:, :I])
+    U = torch.einsum("th,eih->tei", X, W13[:, I:])
+    A = (torch.nn.functional.silu(G) * U).numpy()
+    kk = 3
+    assert slots.size == 20 * kk - 1 and 3 * kk + 1 not in set(slots.tolist())
+    for s, e, row in zip(slots, experts, a):
+        t, j = divmod(int(s), kk)
+        assert e == (ids[t, j] if j < 2 else 5)
+        np.testing.assert_allclose(row, A[t, e], rtol=1e-12, atol=1e-14)
+    # restricted to some tokens: the same rows
+    s2, _, a2 = M.slot_activations(fmt, x, ids, w, num_shared=1, tokens=[4, 11])
+    for s, row in zip(s2, a2):
+        np.testing.assert_allclose(row, a[list(slots).index(s)], rtol=1e-12, atol=1e-15)
