@@ -17,9 +17,10 @@ from synth import gen_weight_f32, bf16_bits
 
 
 def quantize_weight(fmt, w32):
-    """float32 [N, K] -> dict of canonical arrays for one expert."""
+    """float32 [N, K] -> dict of canonical arrays for one expert (the
+    oracle's codecs and quantisers only: NumPy, safe in forked workers)."""
     if fmt == "bf16":
-        return {"w": bf16_bits(torch.from_numpy(np.ascontiguousarray(w32)).to(torch.bfloat16))}
+        return {"w": codecs.bf16_encode_f32(np.ascontiguousarray(w32, dtype=np.float32))}
     if fmt == "mxfp8":
         q, c = quant.mx_quantize(w32, "e4m3")
         return {"w": q, "sf": c}
@@ -116,20 +117,21 @@ def error_summary(y_gpu, y_ref):
 # The L2 input is quantised from the activations: its block scales and
 # element codes are integers decided by floating point.  Both sides decide in
 # float32 (the method's precision), but from activations summed in different
-# orders (MFMA float32 vs float64), so a value lying closer to a decision
-# boundary (an element's rounding midpoint, the amax where a block scale
-# changes) than the float32 evaluation error has two valid quantisations.
-# One flipped element moves its contribution by a whole code step, which for
-# a token with few L2 terms can exceed the bar.  For tokens over the bar, the
-# check recomputes that token with the other valid choice of each such
-# decision (every combination) and accepts it if one meets the bar; every
-# other token is compared as computed.  The evaluation error bound per
-# activation: 2^-19 of the sum of |products| behind g and u (float32
-# accumulation), carried through the activation, plus 2^-18 relative
+# orders and precisions (the GPU's MFMAs vs float64), so a value lying closer
+# to a decision boundary (an element's rounding midpoint, the amax where a
+# block scale changes) than the GPU's evaluation error has two valid
+# quantisations.  One flipped element moves its contribution by a whole code
+# step, which for a token with few L2 terms can exceed the bar.  For tokens
+# over the bar, the check recomputes that token with the other valid choice
+# of each such decision (every combination) and accepts it if one meets the
+# bar; every other token is compared as computed.  The evaluation error bound
+# per activation (_act_error_rows): the float32 accumulation bound of g and u
+# (accumulation_bound), for the MX formats plus the scaled MFMA's own
+# (MX_MFMA_STEP_BOUND), carried through the activation, plus 2^-18 relative
 # (hardware exp and reciprocal).
 
 def accumulation_bound(fmt, K):
-    """Bound, relative to the sum of |products|, on the float32 evaluation
+    """Bound, relative to the sum of |products|, on the float32 rounding
     error of one L1 output (K products): the GPU adds one MFMA K-step's
     products (16 for BF16 and NVFP4, 64 for the scaled MX MFMA) into a
     float32 accumulator at a time, at most one rounding (2^-24 relative) per
@@ -139,14 +141,52 @@ def accumulation_bound(fmt, K):
     return 2.0 * (K // kstep + 4) * 2.0 ** -24
 
 
-def _act_error_rows(fmt, W13, X, act):
+# The scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, the MX formats' L1 and
+# L2) does not add its 64 products at float32 precision: measured with an
+# in-bounds probe on MI355X, one instruction's result is exact while its
+# products span a few binades, and otherwise off by at most 2^-11.06 times
+# the power of two at or below its largest |product| (one instruction, codes
+# drawn over the whole E4M3 range; 2^-12.7 for normal-like data), FP8 x FP8
+# and FP8 x FP4 alike.  The bound taken per 64-wide K-step is 2^-10 times
+# the step's largest |product| (twice the worst measurement).  The BF16 and
+# FP16 MFMAs (BF16 and NVFP4 layers) keep the float32 bound above.
+MX_MFMA_STEP_BOUND = 2.0 ** -10
+
+
+def step_max_products(X, W, step=64):
+    """[n, N]: for every output (row of X, row of W), the sum over its
+    64-wide K-steps of the step's largest |product|."""
+    n, K = X.shape
+    N = W.shape[0]
+    st = K // step
+    Wa = np.abs(W).reshape(N, st, step)
+    out = np.zeros((n, N))
+    for i in range(n):
+        out[i] = (Wa * np.abs(X[i]).reshape(st, step)[None]).max(-1).sum(-1)
+    return out
+
+
+def _act_error_rows(fmt, W13, X, act, exact=False):
     """float64 activations a [n, I] of n slots of one expert (inputs X [n, H])
-    and a bound on their float32 evaluation error: the accumulation bound of
-    g and u carried through the activation, plus 2^-18 relative for the
-    hardware exp and reciprocal."""
+    and a bound on the error with which the GPU evaluates them: the bound
+    on g and u (float32 accumulation; for the MX formats plus the scaled
+    MFMA's per-step bound; with ``exact``, inputs whose L1 sums every path
+    computes exactly, only NVFP4's two float32 scale products and float64
+    noise) carried
+    through the activation, plus 2^-18 relative for the hardware exp and
+    reciprocal."""
     I = W13.shape[0] // 2
     h = X @ W13.T
-    eh = (np.abs(X) @ np.abs(W13).T) * accumulation_bound(fmt, W13.shape[1])
+    if exact:
+        # NVFP4's float32 scale products, and the oracle's own float64
+        # evaluation noise (an exactly zero sum can come out of the float64
+        # matmul as +-1e-17, on either side of zero)
+        eh = np.abs(h) * (4.0 * 2.0 ** -24 if fmt == "nvfp4" else 0.0) + \
+            (np.abs(X) @ np.abs(W13).T) * 2.0 ** -40
+    else:
+        eh = (np.abs(X) @ np.abs(W13).T) * accumulation_bound(fmt, W13.shape[1])
+        if fmt in ("mxfp8", "mxfp4"):
+            eh = eh + MX_MFMA_STEP_BOUND * step_max_products(X, W13)
     f = lambda g, u: activation(g, u, act.get("clamp"), act.get("alpha", 1.0), act.get("beta", 0.0))
     g, u, eg, eu = h[:, :I], h[:, I:], eh[:, :I], eh[:, I:]
     a = f(g, u)
@@ -160,10 +200,12 @@ def _act_error(W13, xs, act, fmt="mxfp8"):
     return a[0], da[0]
 
 
-def slot_l2_inputs(fmt, x_bits, ids, w, *, num_shared=0, expert_start=0, num_local=None, act=None, tokens=None):
+def slot_l2_inputs(fmt, x_bits, ids, w, *, num_shared=0, expert_start=0, num_local=None, act=None, tokens=None,
+                   exact=False):
     """(slots, experts, a, da): the oracle's activations of every live slot
-    (oracle.moe.slot_activations) and a bound on the float32 evaluation
-    error with which the GPU computes them."""
+    (oracle.moe.slot_activations) and a bound on the error with which the
+    GPU computes them (_act_error_rows; ``exact`` for inputs whose L1 sums
+    are exact on the GPU)."""
     from oracle.moe import slot_activations
     act = dict(act or {})
     slots, experts, a = slot_activations(fmt, x_bits, ids, w, num_shared=num_shared, expert_start=expert_start,
@@ -173,7 +215,7 @@ def slot_l2_inputs(fmt, x_bits, ids, w, *, num_shared=0, expert_start=0, num_loc
     for e in np.unique(experts):
         sel = np.nonzero(experts == e)[0]
         X = quantize_x(fmt, np.asarray(x_bits)[slots[sel] // kk])
-        _, da[sel] = _act_error_rows(fmt, dequant_weight(fmt, w, "w13", e), X, act)
+        _, da[sel] = _act_error_rows(fmt, dequant_weight(fmt, w, "w13", e), X, act, exact=exact)
     return slots, experts, a, da
 
 
@@ -199,9 +241,10 @@ def l2_code_check(fmt, codes, scales, a, da, g2=1.0):
     may differ from the oracle's only where the activation lies within its
     error bound of a decision boundary, i.e. where some value within the
     bound is quantised to the GPU's decision.  Returns counts: elements,
-    element flips (codes unlike the oracle's, all of them boundary cases),
-    blocks, scale flips, and ``unexplained`` (differences not so covered;
-    must be 0)."""
+    element flips (values unlike the oracle's, all of them boundary cases),
+    zero-sign flips (+0 against -0 where the value is within its bound of
+    zero), blocks, scale flips, and ``unexplained`` (differences not so
+    covered; must be 0)."""
     a = np.asarray(a, dtype=np.float64)
     da = np.asarray(da, dtype=np.float64)
     n, I = a.shape
@@ -210,7 +253,9 @@ def l2_code_check(fmt, codes, scales, a, da, g2=1.0):
         own = codecs.bf16_encode_f32(a32)
         f32 = lambda v: codecs.bf16_encode_f32(np.asarray(v).astype(np.float32))
         ok = _allowed(codecs.bf16_decode, f32, a, da, codes)
-        return {"elements": int(a.size), "element_flips": int((codes != own).sum()), "blocks": 0,
+        vdiff = codecs.bf16_decode(codes) != codecs.bf16_decode(own)
+        return {"elements": int(a.size), "element_flips": int(vdiff.sum()),
+                "zero_sign_flips": int(((codes != own) & ~vdiff).sum()), "blocks": 0,
                 "scale_flips": 0, "unexplained": int((~ok).sum())}
     grp = 16 if fmt == "nvfp4" else 32
     nb = I // grp
@@ -243,7 +288,10 @@ def l2_code_check(fmt, codes, scales, a, da, g2=1.0):
         ok |= (sv == 0)[..., None] & ((got_c & 0x7) == 0)
     own_q = own_q.reshape(n, nb, grp)
     same_scale = got_s == own_s
-    return {"elements": int(a.size), "element_flips": int(((got_c != own_q) & same_scale[..., None]).sum()),
+    dec = codecs.e4m3_decode if fmt in ("mxfp8", "mxfp4") else codecs.e2m1_decode
+    vdiff = dec(got_c) != dec(own_q)
+    return {"elements": int(a.size), "element_flips": int((vdiff & same_scale[..., None]).sum()),
+            "zero_sign_flips": int(((got_c != own_q) & ~vdiff & same_scale[..., None]).sum()),
             "blocks": int(got_s.size), "scale_flips": int((~same_scale).sum()),
             "unexplained": int((~ok).sum() + (~scale_ok).sum())}
 

@@ -14,7 +14,8 @@ per-expert-group contributions computed in the pool (the layer is a sum over
 slots; the shared expert enters as an always-present id of weight 1).  Also
 checked from the forward's own workspace: the routing metadata and the
 dispatch-quantised x bit-exact at full size, and the L2-input codes of the
-first 64 compared tokens against the oracle's quantiser.
+first 64 compared tokens (16 for the DeepSeek-V3 layer) against the
+oracle's quantiser.
 """
 
 import concurrent.futures
@@ -42,7 +43,7 @@ pytestmark = pytest.mark.gpu
 CASES = [("tiny_bf16", None), ("mixtral_bf16", None), ("dsv3_mxfp8", None), ("nvfp4_zipf", None)] + \
         [("decode_mxfp4", t) for t in DECODE_TOKENS]
 COMPARED_TOKENS = {"dsv3_mxfp8": 256}
-L2_CHECK_TOKENS = 64
+L2_CHECK_TOKENS = {"dsv3_mxfp8": 16}      # else 64
 WORKERS = min(16, os.cpu_count() or 1)
 
 
@@ -118,7 +119,12 @@ def oracle_weights(name, pool):
         cfg = CONFIGS[name]
         E_all = cfg.E + cfg.num_shared
         _WEIGHTS.clear()
-        _WEIGHTS[name] = dict(pool.map(_expert_weights, [(name, e) for e in range(E_all)]))
+        got = {}
+        for e, d in pool.map(_expert_weights, [(name, e) for e in range(E_all)]):
+            got[e] = d
+            if len(got) % 16 == 0:
+                log(f"{name}: {len(got)} of {E_all} experts quantised")
+        _WEIGHTS[name] = got
     return _WEIGHTS[name]
 
 
@@ -232,13 +238,15 @@ def test_fullsize(name, tokens):
         if fmt == "nvfp4":
             m = float(w2in.max())
             g2 = m if m > 0 else 1.0
-        l2_tokens = min(L2_CHECK_TOKENS, sample.size)
+        l2_tokens = min(L2_CHECK_TOKENS.get(name, 64), sample.size)
         jobs = [(name, grp, xb[sample], ids_aug, wts_aug, g2, l2_tokens) for grp in groups]
         ref = np.zeros((sample.size, H))
         l2_parts = []
-        for part, l2 in pool.map(_oracle_part, jobs):
+        for i, (part, l2) in enumerate(pool.map(_oracle_part, jobs)):
             ref += part
             l2_parts.append(l2)
+            if (i + 1) % 8 == 0:
+                log(f"{name}: oracle, {i + 1} of {len(jobs)} expert groups")
     log(f"{name}: oracle done on {sample.size} tokens over {len(groups)} expert groups")
 
     # the layer output
@@ -264,4 +272,5 @@ def test_fullsize(name, tokens):
     record_parity(f"fullsize L2 input {name} T={T} ({l2_tokens} tokens)", **st)
     log(f"{name}: L2-input codes {st}")
     assert st["unexplained"] == 0, st
-    assert st["element_flips"] <= max(2, 1e-3 * st["elements"]), st
+    cap = 5e-3 if fmt in ("mxfp8", "mxfp4") else 1e-3      # as in tests/test_gpu_workspace.py
+    assert st["element_flips"] <= max(2, cap * st["elements"]), st
