@@ -15,12 +15,13 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx950.so")
 
 FMT = {"bf16": 0, "mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
-OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_TOO_LARGE = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "moe_status_string", "moe_get_block_m", "moe_workspace_bytes", "moe_transform_weights",
     "moe_quantize_weights", "moe_quantize_x", "moe_dispatch", "moe_forward", "moe_forward_profiled",
-    "moe_route", "moe_dispatch_scratch_ints", "moe_workspace_layout",
+    "moe_route", "moe_dispatch_scratch_ints", "moe_workspace_layout", "moe_forward_noalloc",
 )
 SCORING = {"softmax": 0, "sigmoid": 1}
 STEPS = ("quant_x", "dispatch", "l1", "l2", "combine")
@@ -85,6 +86,9 @@ def _lib():
         lib.moe_forward.restype = _I
         lib.moe_forward_profiled.argtypes = lib.moe_forward.argtypes + [_P]
         lib.moe_forward_profiled.restype = _I
+        lib.moe_forward_noalloc.argtypes = ([_I] * 9 + [ctypes.POINTER(Activation), ctypes.POINTER(Options)]
+                                            + [_P] * 9 + [ctypes.c_float, _P, _P])
+        lib.moe_forward_noalloc.restype = _I
         lib.moe_route.argtypes = [_I, _I, _I, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P]
         lib.moe_route.restype = _I
         lib.moe_dispatch_scratch_ints.argtypes = [_I, _I, _I, _I]
@@ -299,7 +303,7 @@ def moe_workspace_layout(fmt, num_tokens, hidden, inter, top_k, num_local_expert
 
 def _check_forward_args(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, x, topk_ids,
                         topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale, w2_gscale, out, workspace,
-                        workspace_bytes, norm_gamma):
+                        workspace_bytes, norm_gamma, workspace_required=True):
     _PENDING.clear()
     f = _fmt(fmt)
     T, E = num_tokens, num_local_experts + num_shared
@@ -317,7 +321,8 @@ def _check_forward_args(fmt, num_tokens, hidden, inter, top_k, num_local_experts
     _tensor(w2_gscale, "w2_gscale", dtype=torch.float32, shape=(E,), optional=f != 3)
     _tensor(out, "out", dtype=torch.bfloat16, shape=(T, hidden))
     _tensor(norm_gamma, "norm_gamma", dtype=torch.float32, shape=(hidden,), optional=True)
-    _tensor(workspace, "workspace", min_bytes=workspace_bytes)
+    if workspace_required:
+        _tensor(workspace, "workspace", min_bytes=workspace_bytes)
     _on_gpu()
 
 
@@ -357,6 +362,29 @@ def moe_forward(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_e
     else:
         arr = (ctypes.c_void_p * len(step_events))(*[ctypes.c_void_p(e.cuda_event) for e in step_events])
         _check(_lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
+    return out
+
+
+def moe_forward_noalloc(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,
+                        block_m, act, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k,
+                        w13_gscale, w2_gscale, l2_activation_scale, out, stream=None):
+    """moe_forward without a workspace: the library's fixed per-GPU scratch
+    holds the intermediate buffers (MoEError E_TOO_LARGE if they do not fit).
+    Calls that may overlap on one GPU race for that scratch."""
+    a = None
+    if act is not None:
+        a = ctypes.byref(act if isinstance(act, Activation) else Activation(
+            0, int(act.get("clamp") is not None), float(act.get("clamp") or 0.0),
+            float(act.get("alpha", 1.0)), float(act.get("beta", 0.0))))
+    _PENDING.clear()
+    _check_forward_args(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, x, topk_ids,
+                        topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale, w2_gscale, out, None, None, None,
+                        workspace_required=False)
+    _check(_lib().moe_forward_noalloc(_fmt(fmt), num_tokens, hidden, inter, top_k, expert_start, num_local_experts,
+                                      num_shared, block_m, a, None, _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                                      _ptr(w13_k), _ptr(w13_sf_k), _ptr(w2_k), _ptr(w2_sf_k), _ptr(w13_gscale),
+                                      _ptr(w2_gscale), float(l2_activation_scale), _ptr(out), _stream(stream)),
+           "moe_forward_noalloc")
     return out
 
 

@@ -17,6 +17,12 @@
 #include "common.h"
 #include "launch.h"
 
+// The intermediate buffers of moe_forward_noalloc: one fixed array per GPU
+// (the device code object's own storage, held until the process ends).  In
+// host code its name is a host-side stand-in: only the address
+// hipGetSymbolAddress returns for a device is ever used.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace moe {
 namespace {
 
@@ -25,6 +31,7 @@ struct DeviceInfo {
   bool gfx950 = false;
   int cus = 0;
   bool gemm_ready = false;
+  void* scratch = nullptr;   // this device's address of `scratch`
 };
 constexpr int MAX_DEVICES = 64;
 DeviceInfo g_dev[MAX_DEVICES];
@@ -54,6 +61,23 @@ int device_info(DeviceInfo** info) {
     d.gemm_ready = true;
   }
   *info = &d;
+  return MOE_OK;
+}
+
+// This device's address of the no-allocation scratch, looked up on first use
+// (with the device current).
+int scratch_of(DeviceInfo* d, void** ptr) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!d->scratch) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip = e == hipSuccess ? hipErrorInvalidSymbol : e;
+      return MOE_E_HIP;
+    }
+    d->scratch = p;
+  }
+  *ptr = d->scratch;
   return MOE_OK;
 }
 
@@ -307,6 +331,7 @@ const char* moe_status_string(int status) {
     case MOE_E_UNSUPPORTED: return "unsupported device, format or activation";
     case MOE_E_WORKSPACE: return "workspace too small";
     case MOE_E_HIP: return g_last_hip == hipSuccess ? "HIP error" : hipGetErrorString(g_last_hip);
+    case MOE_E_TOO_LARGE: return "the layer needs more intermediate memory than the fixed no-allocation scratch holds";
     default: return "unknown status";
   }
 }
@@ -464,12 +489,18 @@ int moe_workspace_layout(moe_format_t fmt, int num_tokens, int hidden, int inter
   return MOE_OK;
 }
 
-int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
-                         int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
-                         const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
-                         const void* w13_sf_k, const void* w2_k, const void* w2_sf_k, const float* w13_gscale,
-                         const float* w2_gscale, float l2_activation_scale, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* ev) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward_profiled, and with noalloc the no-allocation variant (the
+// workspace arguments are ignored; the device's scratch array is used).
+int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
+                 int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
+                 const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                 const void* w13_k, const void* w13_sf_k, const void* w2_k, const void* w2_sf_k,
+                 const float* w13_gscale, const float* w2_gscale, float l2_activation_scale, void* out,
+                 void* workspace, size_t workspace_bytes, void* stream, void* const* ev, bool noalloc) {
   // ---- shapes and parameters
   const int shape_status = check_shape(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m);
   if (shape_status != MOE_OK) return shape_status;
@@ -489,7 +520,11 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   if (num_tokens == 0) return MOE_OK;
   // ---- pointers
   const bool scaled = fmt != MOE_FMT_BF16;
-  if (!x || !topk_ids || !topk_weights || !w13_k || !w2_k || !out || !workspace) return MOE_E_INVALID;
+  if (noalloc) {
+    workspace = nullptr;
+    workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  }
+  if (!x || !topk_ids || !topk_weights || !w13_k || !w2_k || !out || (!noalloc && !workspace)) return MOE_E_INVALID;
   if (!aligned16(x) || !aligned16(w13_k) || !aligned16(w2_k) || !aligned16(out) || !aligned16(workspace))
     return MOE_E_INVALID;
   if (scaled && (!w13_sf_k || !w2_sf_k || !aligned16(w13_sf_k) || !aligned16(w2_sf_k))) return MOE_E_INVALID;
@@ -497,15 +532,18 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   if (!gemm_fmt(fmt) || hidden % 256) return MOE_E_UNSUPPORTED;
   Resolved rs;
   const int rst = resolve(fmt, num_tokens, hidden, inter, top_k, num_local_experts, num_shared, block_m,
-                          workspace_bytes, (uint8_t*)workspace, &rs);
-  if (rst != MOE_OK) return rst;
+                          workspace_bytes, nullptr, &rs);
+  if (rst != MOE_OK) return noalloc && rst == MOE_E_WORKSPACE ? MOE_E_TOO_LARGE : rst;
+  DeviceInfo* d;
+  int st = device_info(&d);
+  if (st != MOE_OK) return st;
+  if (noalloc && (st = scratch_of(d, &workspace)) != MOE_OK) return st;
+  rs.w = plan(fmt, num_tokens, hidden, inter, num_local_experts, num_shared, top_k, rs.bm, rs.ks, rs.ks1,
+              (uint8_t*)workspace);
   const int bm = rs.bm, ks = rs.ks, ks1 = rs.ks1;
   const Workspace& w = rs.w;
   const int64_t T = num_tokens, H = hidden, I = inter, kk = top_k + num_shared;
   const int E = num_local_experts + num_shared;
-  DeviceInfo* d;
-  int st = device_info(&d);
-  if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
@@ -633,14 +671,40 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
   return hip_status(hipGetLastError());
 }
 
+}  // namespace
+
+extern "C" {
+
+int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
+                         int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
+                         const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k,
+                         const void* w13_sf_k, const void* w2_k, const void* w2_sf_k, const float* w13_gscale,
+                         const float* w2_gscale, float l2_activation_scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* ev) {
+  return forward_impl(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared, block_m,
+                      act, opts, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale, w2_gscale,
+                      l2_activation_scale, out, workspace, workspace_bytes, stream, ev, false);
+}
+
 int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
                 int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
                 const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights, const void* w13_k, const void* w13_sf_k,
                 const void* w2_k, const void* w2_sf_k, const float* w13_gscale, const float* w2_gscale,
                 float l2_activation_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  return moe_forward_profiled(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared,
-                              block_m, act, opts, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale,
-                              w2_gscale, l2_activation_scale, out, workspace, workspace_bytes, stream, nullptr);
+  return forward_impl(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared, block_m,
+                      act, opts, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale, w2_gscale,
+                      l2_activation_scale, out, workspace, workspace_bytes, stream, nullptr, false);
+}
+
+int moe_forward_noalloc(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k, int expert_start,
+                        int num_local_experts, int num_shared, int block_m, const moe_activation_t* act,
+                        const moe_options_t* opts, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                        const void* w13_k, const void* w13_sf_k, const void* w2_k, const void* w2_sf_k,
+                        const float* w13_gscale, const float* w2_gscale, float l2_activation_scale, void* out,
+                        void* stream) {
+  return forward_impl(fmt, num_tokens, hidden, inter, top_k, expert_start, num_local_experts, num_shared, block_m,
+                      act, opts, x, topk_ids, topk_weights, w13_k, w13_sf_k, w2_k, w2_sf_k, w13_gscale, w2_gscale,
+                      l2_activation_scale, out, nullptr, 0, stream, nullptr, true);
 }
 
 }  // extern "C"

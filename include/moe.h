@@ -36,6 +36,8 @@ extern "C" {
 #define MOE_E_UNSUPPORTED (-2) /* device is not gfx950, or activation/format    */
 #define MOE_E_WORKSPACE (-3)   /* workspace too small                           */
 #define MOE_E_HIP (-4)         /* a HIP call failed (see moe_status_string)     */
+#define MOE_E_TOO_LARGE (-5)   /* the layer needs more intermediate memory than
+                                  moe_forward_noalloc's fixed scratch holds      */
 
 /* Routed-expert precisions: one row each of the page's feature matrix
  * (MegaMoEWeightFormat; module docstring of the DeepGEMM MegaMoE page). */
@@ -310,6 +312,31 @@ typedef struct {
 int moe_workspace_layout(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
                          int num_local_experts, int num_shared, int block_m, size_t workspace_bytes,
                          moe_workspace_layout_t* layout);
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and arguments without a workspace.  The intermediate
+ * results live in one fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES per
+ * GPU, a static device variable of the library that each GPU holds from the
+ * first call on it until the process ends.  Calls whose workspace
+ * (moe_workspace_bytes with the call's block_m, or the BLOCK_M the rule
+ * picks) exceeds it return MOE_E_TOO_LARGE before anything is enqueued; 64
+ * MiB holds decode-sized batches, e.g. up to 256 tokens of a hidden-4096,
+ * intermediate-1536, 128-expert top-8 MXFP4 layer.  Nothing is allocated:
+ * no hipMalloc, no library allocator.  Every call on a GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (different streams, different
+ * host threads) race and must be serialised by the caller; calls on one
+ * stream are ordered and safe.  The scratch keeps the last call's contents;
+ * no step reads anything an earlier call left. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
+                        int expert_start, int num_local_experts, int num_shared, int block_m,
+                        const moe_activation_t* act, const moe_options_t* opts,
+                        const void* x, const int32_t* topk_ids, const float* topk_weights,
+                        const void* w13_k, const void* w13_sf_k,
+                        const void* w2_k, const void* w2_sf_k,
+                        const float* w13_gscale, const float* w2_gscale,
+                        float l2_activation_scale, void* out, void* stream);
 
 #ifdef __cplusplus
 }

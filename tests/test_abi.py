@@ -169,3 +169,31 @@ def test_l1_split_only_for_few_tiles():
     one = moe.moe_workspace_bytes("mxfp4", 1, 4096, 1536, 128, 0, 8, 0)
     two = moe.moe_workspace_bytes("mxfp4", 2, 4096, 1536, 128, 0, 8, 0)
     assert one > 0 and two > one
+
+
+def _noalloc(**kw):
+    lib = moe.lib_handle()
+    a = dict(fmt=0, T=4, H=256, I=256, k=2, nloc=4, nsh=0, bm=0, x=_Fake(), ids=_Fake(), wts=_Fake(),
+             w13=_Fake(), w2=_Fake(), out=_Fake())
+    a.update(kw)
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    return lib.moe_forward_noalloc(a["fmt"], a["T"], a["H"], a["I"], a["k"], 0, a["nloc"], a["nsh"], a["bm"],
+                                   None, None, p(a["x"]), p(a["ids"]), p(a["wts"]), p(a["w13"]), None, p(a["w2"]),
+                                   None, None, None, 1.0, p(a["out"]), None)
+
+
+def test_noalloc_checks_before_touching_a_device():
+    """Invalid arguments, and layers whose intermediate buffers exceed the
+    fixed 64 MiB scratch, are rejected on the host."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _noalloc(H=200) == _lib.E_INVALID
+    assert _noalloc(x=None) == _lib.E_INVALID
+    assert _noalloc(out=_Fake(0x10008)) == _lib.E_INVALID
+    assert _noalloc(T=0) == _lib.OK
+    # 20000 tokens of a hidden-4096 top-2 BF16 layer: far beyond 64 MiB
+    assert _noalloc(T=20000, H=4096, I=1024) == _lib.E_TOO_LARGE
+    assert b"no-allocation" in moe.lib_handle().moe_status_string(_lib.E_TOO_LARGE)
+    # the decode-sized MXFP4 layer at 256 tokens fits (default BLOCK_M)
+    need = moe.moe_workspace_bytes("mxfp4", 256, 4096, 1536, 128, 0, 8,
+                                   moe.moe_get_block_m(256, 128, 0, 8, "mxfp4"))
+    assert need <= _lib.NOALLOC_SCRATCH_BYTES
