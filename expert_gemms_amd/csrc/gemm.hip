@@ -255,9 +255,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   constexpr int READS = FMT == F_NVFP4 ? TM + TN : TM * (FMT == F_BF16 ? 1 : 2) + TN * (FMT == F_MXFP8 ? 2 : 1);
   // scale registers held per stage: NVFP4 two dwords of 4 E4M3 A scales per
   // row block and one dword of B scales per column block; MX one UE8M0 byte
-  // per row / column block and K-step
+  // per row block and K-step (A), and per column block one 16-bit word with
+  // the bytes of both K-steps of its 128-K layout stage (B), the byte chosen
+  // by the MFMA's scale op_sel, so no VALU work splits the word
   constexpr int SA_N = C::NV ? 2 * TM : C::STEPS * TM;
-  constexpr int SB_N = C::NV ? TN : C::STEPS * TN;
+  constexpr int SB_N = TN;
   // L1 passes the weights as the MFMA's first operand: accumulator element v
   // of lane l is then intermediate column 8 (v / 4) + 4 (l / 32) + v % 4 of
   // its 32-column block for sorted row l % 32, so a row's 32 columns sit in
@@ -437,16 +439,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   };
 
   f32x16 acc[TM][TN];   // the tile's accumulators (AGPRs)
-  // Block scales of a stage (in buffer st) of parity PAR.  MX: for each
-  // K-step, the one UE8M0 byte each lane hands its scaled MFMA: the A byte
-  // of the lane's row in K block 2 * (K-step) + g of the stage, and B byte
-  // kl of the lane's 128-K layout stage (kl = the K-step, or for 64-K stages
-  // the stage parity); read as bytes so no VALU work waits on the LDS read.
-  // NVFP4: two E4M3 A scales per row and 64-K group, a dword of four B
-  // scales per column block.
-  auto read_scales = [&](const uint8_t* st, auto parc, uint32_t (&sa)[SA_N], uint32_t (&sb)[SB_N])
+  // Block scales of a stage (in buffer st).  MX: for each K-step, the one
+  // UE8M0 byte each lane hands its scaled MFMA for A: the byte of the lane's
+  // row in K block 2 * (K-step) + g of the stage, read as a byte so no VALU
+  // work waits on the LDS read; for B the lane's 16-bit word of its 128-K
+  // layout stage, whose byte kl (the K-step, or for 64-K stages the stage
+  // parity) the MFMA selects.  NVFP4: two E4M3 A scales per row and 64-K
+  // group, a dword of four B scales per column block.
+  auto read_scales = [&](const uint8_t* st, uint32_t (&sa)[SA_N], uint32_t (&sb)[SB_N])
       __attribute__((always_inline)) {
-    constexpr int PAR = decltype(parc)::value;
     if constexpr (C::SCALED) {
       const uint8_t* Asf = st + G::A_STAGE + G::B_STAGE;
       const uint8_t* Bsf = Asf + G::A_SF_STAGE;
@@ -470,17 +471,17 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         if constexpr (C::NV) {
           sb[tn] = *(const uint32_t*)(Bsf + w * 1024 + tn * 256 + lane * 4);
         } else {
-#pragma unroll
-          for (int ks = 0; ks < C::STEPS; ++ks) {
-            const int kl = C::STEPS == 1 ? PAR : ks;
-            sb[ks * TN + tn] = Bsf[(wn * TN + tn) * 128 + lane * 2 + kl];
-          }
+          sb[tn] = *(const uint16_t*)(Bsf + (wn * TN + tn) * 128 + lane * 2);
         }
       }
     }
   };
-  auto mfmas = [&](int ks, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
+  // MFMAs of K-step ks of a stage; kl: the byte of the B-scale words the MX
+  // K-step takes (op_sel of the weights' scale)
+  auto mfmas = [&](auto ksc, auto klc, const FA (&af)[TM], const FB (&bf)[TN], const uint32_t (&sa)[SA_N],
                    const uint32_t (&sb)[SB_N]) __attribute__((always_inline)) {
+    constexpr int ks = decltype(ksc)::value;
+    constexpr int kl = decltype(klc)::value;
     if constexpr (C::NV) {
       // 64-K group ks: four 16-wide K-steps; sub-step j takes the lane's
       // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
@@ -521,12 +522,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           } else if constexpr (WFIRST) {
             // operand formats: weights FP4 (MXFP4) or FP8, activations FP8
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[tn], af[tm], acc[tm][tn], FMT == F_MXFP4 ? 4 : 0, 0, 0, (int)sb[ks * TN + tn], 0,
+                bf[tn], af[tm], acc[tm][tn], FMT == F_MXFP4 ? 4 : 0, 0, kl, (int)sb[tn], 0,
                 (int)sa[ks * TM + tm]);
           } else {
             acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[ks * TM + tm], 0,
-                (int)sb[ks * TN + tn]);
+                af[tm], bf[tn], acc[tm][tn], 0, FMT == F_MXFP4 ? 4 : 0, 0, (int)sa[ks * TM + tm], kl,
+                (int)sb[tn]);
           }
         }
       }
@@ -610,7 +611,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     uint32_t sa4[SA_N] = {}, sb2[SB_N] = {}, sa4n[SA_N] = {}, sb2n[SB_N] = {};
     {
       const uint8_t* st0 = smem + cur * G::STAGE;
-      read_scales(st0, IC<0>{}, sa4, sb2);
+      read_scales(st0, sa4, sb2);
       load_frags<FMT, TM, TN, C>(st0, st0 + G::A_STAGE, 0, wm, wn, lane, af[0], bfr[0]);
     }
     constexpr int MF = TM * TN * (C::NV ? 4 : 1);   // MFMAs per K-step
@@ -638,7 +639,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         constexpr int r0 = (RB + ks) & 1, r1 = (RB + ks + 1) & 1;
         load_frags<FMT, TM, TN, C>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
         issue(IC<lo>{}, IC<hi>{}, tf, js, fill);
-        mfmas(ks, af[r0], bfr[r0], sa4, sb2);
+        mfmas(IC<ks>{}, IC<ks>{}, af[r0], bfr[r0], sa4, sb2);
         boundary_hint<READS, MF, hi - lo>();
       });
       constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies of s+NBUF-1 issued so far
@@ -651,12 +652,13 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         wait_vmcnt<(G::NBUF - 3) * G::CPS + LAST>();
         lds_barrier();
         const uint8_t* nx = smem + nxt * G::STAGE;
-        // with one K-step per stage, RB is the stage's parity
-        read_scales(nx, IC<(RB + 1) & 1>{}, sa4n, sb2n);
+        read_scales(nx, sa4n, sb2n);
         load_frags<FMT, TM, TN, C>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
       }
       issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
-      mfmas(C::STEPS - 1, af[rl], bfr[rl], sa4, sb2);
+      // with one K-step per stage, RB is the stage's parity: the half of
+      // the 128-K layout stage whose B-scale byte the K-step takes
+      mfmas(IC<C::STEPS - 1>{}, IC<C::STEPS == 1 ? (RB & 1) : C::STEPS - 1>{}, af[rl], bfr[rl], sa4, sb2);
       boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + SB_N : 0), MF, G::CPS - LAST>();
       if constexpr (!LASTS) {
 #pragma unroll
@@ -717,20 +719,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     } else {
       // NVFP4 L2: w2's expert scale times the L2 input's global scale
       const float alpha2 = C::NV && LAYER == 2 ? __builtin_bit_cast(float, sload(p.w_gs + e)) * p.l2_scale : 1.0f;
-      // the slots of the lane's 16 rows per row block, from the row buffer
+      // the slots of the lane's 16 rows of each row block, from the row
+      // buffer (one row block at a time)
       const int32_t* rslot = (const int32_t*)(smem + G::ROWS_OFF + ta.par * 1024);
-      int slots[TM][16];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 s4 = *(const int4*)(rslot + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
-          slots[tm][4 * q] = s4.x;
-          slots[tm][4 * q + 1] = s4.y;
-          slots[tm][4 * q + 2] = s4.z;
-          slots[tm][4 * q + 3] = s4.w;
-        }
-      }
       // block-scaled L2 with K unsplit: BF16 rows (the output dtype the
       // combine reads), stored non-temporally (written once, read once by
       // the combine, so they need not displace the weights from the
@@ -738,9 +729,18 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const bool o16 = FMT != F_BF16 && LAYER == 2 && p.o_bf16;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
+        int slots[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int4 s4 = *(const int4*)(rslot + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
+          slots[4 * q] = s4.x;
+          slots[4 * q + 1] = s4.y;
+          slots[4 * q + 2] = s4.z;
+          slots[4 * q + 3] = s4.w;
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int slot = slots[tm][v];
+          const int slot = slots[v];
           if (slot < 0) continue;
           const int64_t col = (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
           if (o16) {
