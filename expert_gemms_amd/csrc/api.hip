@@ -161,9 +161,26 @@ bool valid_fmt(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_MXFP8 || f == M
 bool gemm_fmt(int f) { return valid_fmt(f); }
 
 // Expected padded rows of one group whose row count c is near-Poisson with
-// mean m (normal approximation): E[ceil(c / bm)] * bm = bm * sum_j P(c > j bm).
+// mean m: E[ceil(c / bm)] * bm = bm * sum_j P(c > j bm).  The Poisson tail is
+// summed directly below a mean of 64 (decode batches, where most experts get
+// no row and the normal approximation miscounts the experts that get one),
+// and approximated by the normal distribution above.
 double expected_padded(double m, int bm) {
   if (m <= 0.0) return 0.0;
+  if (m < 64.0) {
+    double tiles = 0.0, pmf = std::exp(-m), cdf = 0.0;   // pmf: P(c = n)
+    int n = 0;
+    for (int j = 0;; ++j) {
+      for (; n <= j * bm; ++n) {
+        cdf += pmf;
+        pmf *= m / (n + 1);
+      }
+      const double tail = 1.0 - cdf;
+      if (tail < 1e-12) break;
+      tiles += tail;
+    }
+    return tiles * bm;
+  }
   const double sd = std::sqrt(m);
   double tiles = 0.0;
   for (int j = 0;; ++j) {
@@ -561,10 +578,11 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   // metadata (a2) in one launch, timed as the quantisation step
   const bool mx = fmt == MOE_FMT_MXFP8 || fmt == MOE_FMT_MXFP4;
   const bool fused = mx && (!w.block_counts || dispatch_single_wg(num_tokens, top_k, num_shared));
+  bool planes = false;   // the fused launch also wrote the L1 scale planes
   if (fused)
-    launch_dispatch_quant_mx(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts,
-                             w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, xin, (int)H, w.xq,
-                             w.xq_sf, s);
+    planes = launch_dispatch_quant_mx(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm,
+                                      w.counts, w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, xin,
+                                      (int)H, w.xq, w.xq_sf, w.a1_sf, w.sf_plane, s);
   else if (mx)
     launch_quant_mx(false, false, T, (int)H, xin, w.xq, w.xq_sf, s);
   else if (fmt == MOE_FMT_NVFP4)
@@ -577,7 +595,7 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
                     w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, w.block_counts, s);
   const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
   const int64_t grp = nv ? 16 : 32;          // elements per block scale
-  if (scaled) {
+  if (scaled && !planes) {
     // the dispatch-quantised x scales in the sorted rows' plane layout
     // (padding rows: scale 1)
     const int64_t M = T * kk + (int64_t)E * (bm - 1);

@@ -157,23 +157,153 @@ k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int sta
               meta);
 }
 
+// Sorted rows of the slots [s0, s1) (whole tokens) without the routing
+// metadata, for a workgroup that needs them but does not build them: every
+// slot's expert is counted (LDS atomics; cnt_before counts the slots before
+// s0), the BLOCK_M-padded groups are laid out as dispatch_wg lays them out
+// (gstart: each group's first row), and the slots of [s0, s1) are ranked in
+// slot order from gstart + cnt_before, the same stable order, so row_of[s -
+// s0] equals the slot_row[s] the dispatch writes (-1: dropped).
+constexpr int LOCAL_SLOTS = 4096;
+
+__device__ __forceinline__ void local_rows(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start,
+                                           int n_loc, int bm, int nbits, int s0, int s1, int* cnt_all,
+                                           int* cnt_before, int* gstart, int* row_of) {
+  __shared__ int wave_tot[DISPATCH_WAVES];
+  const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
+  const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
+  for (int e = tid; e < E; e += DISPATCH_THREADS) cnt_all[e] = cnt_before[e] = 0;
+  __syncthreads();
+  for (int s = tid; s < S; s += DISPATCH_THREADS) {
+    const int e = slot_expert(topk_ids, s, kk, k, start, n_loc);
+    if (e >= 0) {
+      atomicAdd(&cnt_all[e], 1);
+      if (s < s0) atomicAdd(&cnt_before[e], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the padded group sizes over experts (one per thread)
+  const int v = tid < E ? (cnt_all[tid] + bm - 1) / bm * bm : 0;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (l >= d) incl += o;
+  }
+  if (l == WAVE - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int ww = 0; ww < w; ++ww) wbase += wave_tot[ww];
+  if (tid < E) {
+    gstart[tid] = wbase + incl - v;
+    cnt_before[tid] += wbase + incl - v;      // next row of expert tid for the slots from s0 on
+  }
+  __syncthreads();
+  // wave 0 ranks [s0, s1) in 64-slot batches (as wave_scatter does)
+  if (w == 0) {
+    const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+    for (int b = s0; b < s1; b += WAVE) {
+      const int s = b + l;
+      const bool live = s < s1;
+      const int e = live ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+      const uint64_t m = match_mask(e, nbits);
+      if (e >= 0) row_of[s - s0] = cnt_before[e] + __builtin_popcountll(m & lt_mask);
+      else if (live) row_of[s - s0] = -1;
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && __builtin_ctzll(m) == l) cnt_before[e] += __builtin_popcountll(m);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+}
+
 // The single-workgroup dispatch and the MX dispatch quantisation of x (E4M3
-// codes, BF16 input) in one launch: the two are independent, so workgroup 0
-// builds the routing metadata while workgroups 1 .. quantise x, one MX block
-// per thread; this saves a launch on decode-sized batches.
+// codes, BF16 input) in one launch: workgroup 0 builds the routing metadata
+// while workgroups 1 .. nq quantise x, one MX block per thread (QB blocks
+// per workgroup with a1_sf, which spreads the scale scatter over more CUs;
+// the rest of the workgroup's threads only help to count).  With a1_sf
+// the launch also writes the L1 GEMM's scale planes that launch_gather_sf
+// would: the quantising workgroups place each block scale at a1_sf[kb *
+// plane + row] for every sorted row of its token (rows from local_rows), and
+// workgroups nq + 1 .. each fill the padding rows of FILL_PLANES planes with
+// UE8M0 1.0, lanes on consecutive rows.  Real and padding rows are disjoint,
+// so no two workgroups write one byte.  This saves two launches on
+// decode-sized batches.
+constexpr int FILL_PLANES = 4;
+constexpr int QB = 256;
+
 __global__ void __launch_bounds__(DISPATCH_THREADS)
 k_dispatch_quant_mx(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                     int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
                     int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta, const void* __restrict__ x,
-                    int64_t nblocks, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                    int nkb, int64_t nblocks, int nq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                    uint8_t* __restrict__ a1_sf, int64_t plane) {
   if (blockIdx.x == 0) {
     dispatch_wg(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert,
                 meta);
     return;
   }
-  const int64_t b = (int64_t)(blockIdx.x - 1) * DISPATCH_THREADS + threadIdx.x;
-  if (b < nblocks) quant_mx_block<false, false>(x, b, codes, scales);
+  const int q = blockIdx.x - 1, tid = threadIdx.x;
+  if (!a1_sf) {
+    const int64_t b = (int64_t)q * DISPATCH_THREADS + tid;
+    if (b < nblocks) quant_mx_block<false, false>(x, b, codes, scales);
+    return;
+  }
+  const int64_t b0 = (int64_t)q * QB, b = b0 + tid;
+  __shared__ int cnt_all[MAX_LOCAL_EXPERTS], next_row[MAX_LOCAL_EXPERTS], gstart[MAX_LOCAL_EXPERTS];
+  __shared__ int row_of[LOCAL_SLOTS];
+  const int kk = k + n_sh, E = n_loc + n_sh;
+  if (q < nq) {
+    // this workgroup's tokens [t0, t1)
+    const int t0 = (int)(b0 / nkb);
+    const int t1 = (int)min<int64_t>((b0 + QB - 1) / nkb + 1, T);
+    local_rows(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, t0 * kk, t1 * kk, cnt_all, next_row, gstart, row_of);
+    if (tid < QB && b < nblocks) {
+      const int c = quant_mx_block<false, false>(x, b, codes, scales);
+      const int t = (int)(b / nkb), kb = (int)(b % nkb);
+      for (int j = 0; j < kk; ++j) {
+        const int r = row_of[(t - t0) * kk + j];
+        if (r >= 0) a1_sf[kb * plane + r] = (uint8_t)c;
+      }
+    }
+    return;
+  }
+  // padding rows of planes [kb0, kb1): expert e pads rows [gstart + count,
+  // gstart + padded); pad_end (in row_of) is the inclusive scan of the
+  // padding counts, and padding row i of the plane belongs to the first
+  // expert whose pad_end exceeds i
+  __shared__ int wave_tot[DISPATCH_WAVES];
+  local_rows(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, 0, 0, cnt_all, next_row, gstart, row_of);
+  const int w = tid / WAVE, l = tid % WAVE;
+  const int pad = tid < E ? (cnt_all[tid] + bm - 1) / bm * bm - cnt_all[tid] : 0;
+  int incl = pad;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (l >= d) incl += o;
+  }
+  if (l == WAVE - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int wbase = 0, P = 0;
+  for (int ww = 0; ww < DISPATCH_WAVES; ++ww) {
+    if (ww < w) wbase += wave_tot[ww];
+    P += wave_tot[ww];
+  }
+  if (tid < E) row_of[tid] = wbase + incl;
+  __syncthreads();
+  const int kb0 = (q - nq) * FILL_PLANES, kb1 = min(kb0 + FILL_PLANES, nkb);
+  for (int i = tid; i < P; i += DISPATCH_THREADS) {
+    int lo = 0, hi = E - 1;                    // first e with pad_end[e] > i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (row_of[mid] > i) hi = mid;
+      else lo = mid + 1;
+    }
+    const int n = cnt_all[lo], pad_lo = (n + bm - 1) / bm * bm - n;
+    const int r = gstart[lo] + n + (i - (row_of[lo] - pad_lo));
+    for (int kb = kb0; kb < kb1; ++kb) a1_sf[kb * plane + r] = 127;
+  }
 }
 
 // Many-workgroup dispatch for large slot counts: the same metadata in three
@@ -317,18 +447,24 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
 
 bool dispatch_single_wg(int T, int k, int n_sh) { return (int64_t)T * (k + n_sh) < DISPATCH_MANY_MIN_SLOTS; }
 
-void launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                               int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
                               int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
-                              uint8_t* scales, hipStream_t stream) {
+                              uint8_t* scales, uint8_t* a1_sf, int64_t plane, hipStream_t stream) {
   const int E = n_loc + n_sh;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const int64_t nblocks = (int64_t)T * (H / 32);
-  const unsigned nq = (unsigned)((nblocks + DISPATCH_THREADS - 1) / DISPATCH_THREADS);
-  hipLaunchKernelGGL(k_dispatch_quant_mx, dim3(1 + nq), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh,
-                     start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta, x, nblocks,
-                     codes, scales);
+  const int nkb = H / 32;
+  const int64_t nblocks = (int64_t)T * nkb;
+  // a workgroup's QB blocks touch at most (QB - 1) / nkb + 2 tokens
+  const bool planes = a1_sf && ((QB - 1) / nkb + 2) * (k + n_sh) <= LOCAL_SLOTS;
+  const int per = planes ? QB : DISPATCH_THREADS;
+  const unsigned nq = (unsigned)((nblocks + per - 1) / per);
+  const unsigned nf = planes ? (unsigned)((nkb + FILL_PLANES - 1) / FILL_PLANES) : 0;
+  hipLaunchKernelGGL(k_dispatch_quant_mx, dim3(1 + nq + nf), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k,
+                     n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta, x, nkb,
+                     nblocks, (int)nq, codes, scales, planes ? a1_sf : nullptr, plane);
+  return planes;
 }
 
 // Block scales of the L1 A operand in the GEMM's layout: one plane per

@@ -153,9 +153,9 @@ __device__ __forceinline__ float load_elem(const void* src, int64_t i) {
 // MX block b (32 elements of src): its UE8M0 scale and element codes,
 // written unpacked for E4M3 and two per byte for E2M1, by the hardware
 // converts (equal to the software encoders here: the scaled block maximum is
-// at most the format's largest value).
+// at most the format's largest value).  Returns the scale code.
 template <bool F32, bool FP4>
-__device__ __forceinline__ void quant_mx_block(const void* __restrict__ src, int64_t b, uint8_t* __restrict__ codes,
+__device__ __forceinline__ int quant_mx_block(const void* __restrict__ src, int64_t b, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales) {
 #pragma clang fp contract(off)
   float v[32];
@@ -188,6 +188,7 @@ __device__ __forceinline__ void quant_mx_block(const void* __restrict__ src, int
     *(uint4*)(codes + b * 32) = make_uint4(w[0], w[1], w[2], w[3]);
     *(uint4*)(codes + b * 32 + 16) = make_uint4(w[4], w[5], w[6], w[7]);
   }
+  return c;
 }
 
 }  // namespace moe

@@ -72,11 +72,14 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
 // True when launch_dispatch runs the single-workgroup kernel.
 bool dispatch_single_wg(int T, int k, int n_sh);
 // That kernel and the MX dispatch quantisation of BF16 x [T, H] (E4M3 codes,
-// UE8M0 scales, as launch_quant_mx(false, false, ...)) in one launch.
-void launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
+// UE8M0 scales, as launch_quant_mx(false, false, ...)) in one launch; with
+// a1_sf, the same launch also writes the scale planes launch_gather_sf would
+// (fill 127) when the slots of a quantising workgroup's tokens fit its LDS,
+// and returns whether it did.
+bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                               int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
                               int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
-                              uint8_t* scales, hipStream_t stream);
+                              uint8_t* scales, uint8_t* a1_sf, int64_t plane, hipStream_t stream);
 
 // Sum of the K parts of a split L1 GEMM (a.o, a.ksplit, a.o_split), then its
 // activation and L2-input quantisation into (a.c, a.c_sf).
