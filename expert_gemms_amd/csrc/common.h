@@ -103,28 +103,27 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
-// An E4M3 block scale as two FP16 copies of 2^-8 times its value, built from
-// its bits: E4M3's exponents and 3 mantissa bits fit FP16 (bias 15 - 7 = 8
-// absorbed by the 2^-8), its subnormals become FP16 subnormals, so this is
-// exact.  The packed FP4 convert supplies the 2^8.
-__device__ __forceinline__ f16x2 nv_scale(uint32_t c) {
-  const uint32_t h = ((c & 0x7Fu) << 7) | ((c & 0x80u) << 8);
-  return __builtin_bit_cast(f16x2, h | (h << 16));
+// Two E4M3 block scales (bytes 2 W and 2 W + 1 of c) as FP16 by the
+// hardware convert: every E4M3 value, subnormals included (down to 2^-9),
+// is an FP16 normal number, so this is exact.
+template <bool W>
+__device__ __forceinline__ f16x2 nv_scales(uint32_t c) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, W);
 }
 
 // Eight packed E2M1 values (one dword, two per byte, element 2b in the low
-// nibble of byte b) times an E4M3 block scale -> eight FP16 values: the
-// convert gives each value times 2^8 (it applies the power of two of its
-// float32 scale), the packed FP16 multiply by the scale's 2^-8 copy gives
-// the product.  E2M1 x E4M3 has at most 6 significant bits and magnitudes in
-// [2^-10, 2688], so both steps are exact in FP16.  The vector is assembled by
-// bit casts of whole dwords.
+// nibble of byte b) times an E4M3 block scale s (both halves of s hold it)
+// -> eight FP16 values: the convert gives the E2M1 values, the packed FP16
+// multiply the products.  E2M1 x E4M3 has at most 6 significant bits and
+// magnitudes in [2^-10, 2688], so both steps are exact in FP16.  (The
+// multiply takes s from one half of a pair of scales through its op_sel.)
+// The vector is assembled by bit casts of whole dwords.
 __device__ __forceinline__ f16x8 nvfp4_to_f16x8(int packed, f16x2 s) {
   const uint32_t v = (uint32_t)packed;
-  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 256.0f, 0) * s;
-  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 256.0f, 1) * s;
-  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 256.0f, 2) * s;
-  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 256.0f, 3) * s;
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0) * s;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1) * s;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2) * s;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3) * s;
   const i32x4 w = {__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1), __builtin_bit_cast(int, p2),
                    __builtin_bit_cast(int, p3)};
   return __builtin_bit_cast(f16x8, w);

@@ -487,13 +487,20 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // values [8j, 8j+8) (K = 32g + 8j + i), in block 2g + j/2 of the
       // group: byte 2g + j/2 of the row's A-scale dword, byte 2ks + j/2 of
       // the lane's B-scale dword
+      // the row's (column's) two block scales of the group as FP16, one
+      // convert each: A bytes 0, 1 of its dword, B bytes 2ks, 2ks + 1
+      f16x2 pa[TM], pb[TN];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) pa[tm] = nv_scales<false>(sa[ks * TM + tm]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) pb[tn] = nv_scales<ks == 1>(sb[tn]);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {            // the two 16-blocks of the lane's 32 values
         f16x2 ssa[TM], ssb[TN];
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) ssa[tm] = nv_scale((sa[ks * TM + tm] >> (8 * h)) & 0xFF);
+        for (int tm = 0; tm < TM; ++tm) ssa[tm] = h ? pa[tm].yy : pa[tm].xx;
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) ssb[tn] = nv_scale((sb[tn] >> (8 * (2 * ks + h))) & 0xFF);
+        for (int tn = 0; tn < TN; ++tn) ssb[tn] = h ? pb[tn].yy : pb[tn].xx;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int j = 2 * h + jj;
