@@ -12,7 +12,10 @@ import threading
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_gfx950.so")
+# MOE_LIBRARY names another build of the same library (the tests' host-
+# sanitizer build); unset, the in-tree library is loaded
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libmoe_gfx950.so")
 
 FMT = {"bf16": 0, "mxfp8": 1, "mxfp4": 2, "nvfp4": 3}
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_TOO_LARGE = 0, -1, -2, -3, -4, -5

@@ -41,7 +41,11 @@ extern "C" {
 
 /* Routed-expert precisions: one row each of the page's feature matrix
  * (MegaMoEWeightFormat; module docstring of the DeepGEMM MegaMoE page). */
-typedef enum {
+/* Weight formats.  moe_format_t is a plain int so that any value a caller
+ * passes is well defined on both sides of the ABI; values other than these
+ * four are rejected with MOE_E_INVALID. */
+typedef int moe_format_t;
+enum {
   MOE_FMT_BF16 = 0,  /* BF16 weights, BF16 dispatch, BF16 L2 input            */
   MOE_FMT_MXFP8 = 1, /* E4M3 weights + UE8M0 per 1x32; MXFP8 activations      */
   MOE_FMT_MXFP4 = 2, /* E2M1 weights (2 per byte) + UE8M0 per 1x32; MXFP8
@@ -49,7 +53,7 @@ typedef enum {
   MOE_FMT_NVFP4 = 3  /* E2M1 weights + E4M3 per 1x16 + per-expert FP32 global;
                         NVFP4 activations: per-token FP32 scale at dispatch,
                         one global scale for every L2 input                  */
-} moe_format_t;
+};
 
 /* Gated activation fused into the L1 epilogue (MegaMoEActivation on the
  * DeepGEMM MegaMoE page): swiglu = gate * sigmoid(alpha * gate) * (up + beta)
