@@ -176,7 +176,7 @@ double expected_padded(double m, int bm) {
         pmf *= m / (n + 1);
       }
       const double tail = 1.0 - cdf;
-      if (tail < 1e-12) break;
+      if (tail < 1e-12 || n > 4096) break;   // (the tail is negligible long before n = 4096 for m < 64)
       tiles += tail;
     }
     return tiles * bm;
