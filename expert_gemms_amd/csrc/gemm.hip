@@ -777,16 +777,30 @@ template <int FMT>
 __global__ void __launch_bounds__(64) k_l1_finish(const GemmArgs p, const int32_t* __restrict__ slot_row,
                                                   const int32_t* __restrict__ tile_expert, int bm) {
   const int s = blockIdx.x;
-  const int m = slot_row[s];
-  if (m < 0) return;
   const int lane = threadIdx.x, l32 = lane & 31;
   const int icol = blockIdx.y * 64 + lane;
   const int nc = (icol >> 5) * 64 + (icol & 31);   // gate column; up is 32 further
+  // the parts (at most 4, the split rule's limit) are loaded together with
+  // the slot's row, so the launch waits out one load latency, not two; a
+  // dropped slot's parts, never written, are loaded and not used
+  float gp[4], up[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < p.ksplit) {
+      const float* row = p.o + ks * p.o_split + (int64_t)s * p.N;
+      gp[ks] = row[nc];
+      up[ks] = row[nc + 32];
+    }
+  }
+  const int m = slot_row[s];
+  if (m < 0) return;
   float g = 0.0f, u = 0.0f;
-  for (int ks = 0; ks < p.ksplit; ++ks) {
-    const float* row = p.o + ks * p.o_split + (int64_t)s * p.N;
-    g += row[nc];
-    u += row[nc + 32];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < p.ksplit) {
+      g += gp[ks];
+      u += up[ks];
+    }
   }
   if constexpr (FMT == F_NVFP4) {
     const float alpha = p.a_tok[s / p.kk] * p.w_gs[tile_expert[m / bm]];
