@@ -93,6 +93,7 @@ struct Workspace {
   int32_t* sorted_slot;
   int32_t* slot_row;
   int32_t* tile_expert;
+  int32_t* tile_info;      // GemmArgs::tile_info
   int32_t* block_counts;   // the many-workgroup dispatch's per-chunk counts
   uint8_t* xq;        // dispatch-quantised x codes
   uint8_t* xq_sf;     // its block scales, [T, H / block]
@@ -121,6 +122,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
   w.sorted_slot = (int32_t*)take(M * 4);
   w.slot_row = (int32_t*)take(S * 4);
   w.tile_expert = (int32_t*)take(M / bm * 4 + 4);
+  w.tile_info = (int32_t*)take(M / bm * 16 + 16);
   w.block_counts = (int32_t*)take(dispatch_scratch_ints(S, (int)E) * 4);
   w.xq = w.xq_sf = w.a1_sf = w.a2 = w.a2_sf = nullptr;
   w.xs = nullptr;
@@ -441,7 +443,7 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start, in
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, block_m, counts, offsets,
-                  sorted_slot, slot_row, tile_expert, nullptr, block_counts, (hipStream_t)stream);
+                  sorted_slot, slot_row, tile_expert, nullptr, nullptr, block_counts, (hipStream_t)stream);
   return hip_status(hipGetLastError());
 }
 
@@ -581,7 +583,8 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   bool planes = false;   // the fused launch also wrote the L1 scale planes
   if (fused)
     planes = launch_dispatch_quant_mx(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm,
-                                      w.counts, w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, xin,
+                                      w.counts, w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.tile_info,
+                                      w.meta, xin,
                                       (int)H, w.xq, w.xq_sf, w.a1_sf, w.sf_plane, s);
   else if (mx)
     launch_quant_mx(false, false, T, (int)H, xin, w.xq, w.xq_sf, s);
@@ -592,7 +595,7 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   mark(2 * MOE_STEP_DISPATCH);
   if (!fused)
     launch_dispatch(topk_ids, num_tokens, top_k, num_shared, expert_start, num_local_experts, bm, w.counts,
-                    w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.meta, w.block_counts, s);
+                    w.offsets, w.sorted_slot, w.slot_row, w.tile_expert, w.tile_info, w.meta, w.block_counts, s);
   const bool nv = fmt == MOE_FMT_NVFP4, fp4 = fmt == MOE_FMT_MXFP4 || nv;
   const int64_t grp = nv ? 16 : 32;          // elements per block scale
   if (scaled && !planes) {
@@ -635,6 +638,7 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   g.sorted_slot = w.sorted_slot;
   g.offsets = w.offsets;
   g.tile_expert = w.tile_expert;
+  g.tile_info = w.tile_info;
   g.row_scale = w.row_tok;
   g.meta = w.meta;
   g.kk = (int)kk;

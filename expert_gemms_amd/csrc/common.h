@@ -164,6 +164,11 @@ __device__ __forceinline__ int sload(const void* p) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   return v;
 }
+__device__ __forceinline__ i32x4 sload4(const void* p) {
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+  return v;
+}
 __device__ __forceinline__ i32x8 sload8(const void* p) {
   i32x8 v;
   asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");

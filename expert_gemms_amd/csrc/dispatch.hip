@@ -82,13 +82,34 @@ __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ topk_id
   }
 }
 
+// The tile -> expert tables for BLOCK_M blocks [0, nblocks), the blocks
+// spread over the workgroup's threads: block tb belongs to the last expert
+// whose group starts at or before row tb * bm (empty groups share their
+// start with the next group and come before it).  s_off: the groups' first
+// rows [E + 1] in LDS.
+__device__ __forceinline__ void tile_tables(const int* s_off, int E, int bm, int nblocks,
+                                            int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_info) {
+  for (int tb = threadIdx.x; tb < nblocks; tb += DISPATCH_THREADS) {
+    const int r = tb * bm;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    tile_expert[tb] = lo;
+    if (tile_info) *(int4*)(tile_info + 4 * tb) = make_int4(lo, s_off[lo] / bm, (s_off[lo + 1] - s_off[lo]) / bm, 0);
+  }
+}
+
 __device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start,
                                             int n_loc, int bm, int nbits, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
                                             int32_t* __restrict__ slot_row, int32_t* __restrict__ tile_expert,
-                                            int32_t* __restrict__ meta) {
+                                            int32_t* __restrict__ tile_info, int32_t* __restrict__ meta) {
   __shared__ int hist[DISPATCH_WAVES][MAX_LOCAL_EXPERTS];
   __shared__ int wave_tot[DISPATCH_WAVES];
+  __shared__ int s_off[MAX_LOCAL_EXPERTS + 1];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
   const int kk = k + n_sh, E = n_loc + n_sh, S = T * kk;
 
@@ -127,10 +148,12 @@ __device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids
   for (int ww = 0; ww < DISPATCH_WAVES; ++ww) total += wave_tot[ww];
   if (tid < E) {
     offsets[tid] = off;
+    s_off[tid] = off;
     for (int ww = 0; ww < DISPATCH_WAVES; ++ww) hist[ww][tid] += off;
   }
   if (tid == 0) {
     offsets[E] = total;
+    s_off[E] = total;
     if (meta) {
       meta[0] = total / bm;   // number of BLOCK_M tiles
       meta[1] = total;        // padded rows
@@ -141,20 +164,19 @@ __device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids
   // pass 3: stable scatter
   wave_scatter(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
 
-  // padding rows and the tile -> expert table
-  if (tid < E) {
+  // padding rows and the tile -> expert tables
+  if (tid < E)
     for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
-    for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
-  }
+  tile_tables(s_off, E, bm, total / bm, tile_expert, tile_info);
 }
 
 __global__ void __launch_bounds__(DISPATCH_THREADS)
 k_dispatch(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc,
            int bm, int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
            int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
-           int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+           int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_info, int32_t* __restrict__ meta) {
   dispatch_wg(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert,
-              meta);
+              tile_info, meta);
 }
 
 // Sorted rows of the slots [s0, s1) (whole tokens) without the routing
@@ -236,12 +258,13 @@ __global__ void __launch_bounds__(DISPATCH_THREADS)
 k_dispatch_quant_mx(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                     int nbits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row,
-                    int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta, const void* __restrict__ x,
+                    int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_info, int32_t* __restrict__ meta,
+                    const void* __restrict__ x,
                     int nkb, int64_t nblocks, int nq, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                     uint8_t* __restrict__ a1_sf, int64_t plane) {
   if (blockIdx.x == 0) {
     dispatch_wg(topk_ids, T, k, n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert,
-                meta);
+                tile_info, meta);
     return;
   }
   const int q = blockIdx.x - 1, tid = threadIdx.x;
@@ -340,8 +363,9 @@ k_dispatch_count(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, i
 __global__ void __launch_bounds__(DISPATCH_THREADS)
 k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, int32_t* __restrict__ counts,
                 int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
-                int32_t* __restrict__ tile_expert, int32_t* __restrict__ meta) {
+                int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_info, int32_t* __restrict__ meta) {
   __shared__ int wave_tot[DISPATCH_WAVES];
+  __shared__ int s_off[MAX_LOCAL_EXPERTS + 1];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
   // the chunks' counts of expert tid, 16 loads in flight at a time (a
   // load-add-store chain per chunk would wait out each load's latency)
@@ -385,15 +409,18 @@ k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, 
         if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = b[i] + off;
     }
     for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
-    for (int tb = off / bm; tb < (off + v) / bm; ++tb) tile_expert[tb] = tid;
+    s_off[tid] = off;
   }
   if (tid == 0) {
     offsets[E] = total;
+    s_off[E] = total;
     if (meta) {
       meta[0] = total / bm;
       meta[1] = total;
     }
   }
+  __syncthreads();
+  tile_tables(s_off, E, bm, total / bm, tile_expert, tile_info);
 }
 
 __global__ void __launch_bounds__(DC_WAVES * WAVE)
@@ -426,7 +453,8 @@ int64_t dispatch_scratch_ints(int64_t S, int E) { return (S + DCHUNK - 1) / DCHU
 
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                     int32_t* tile_expert, int32_t* meta, int32_t* block_counts, hipStream_t stream) {
+                     int32_t* tile_expert, int32_t* tile_info, int32_t* meta, int32_t* block_counts,
+                     hipStream_t stream) {
   int E = n_loc + n_sh;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -436,20 +464,21 @@ void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start,
     hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(DC_WAVES * WAVE), 0, stream, topk_ids, T, k, n_sh, start,
                        n_loc, nbits, block_counts);
     hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(DISPATCH_THREADS), 0, stream, nchunks, E, bm, block_counts,
-                       counts, offsets, sorted_slot, tile_expert, meta);
+                       counts, offsets, sorted_slot, tile_expert, tile_info, meta);
     hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(DC_WAVES * WAVE), 0, stream, topk_ids, T, k, n_sh,
                        start, n_loc, nbits, block_counts, sorted_slot, slot_row);
     return;
   }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k, n_sh, start,
-                     n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta);
+                     n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, tile_info, meta);
 }
 
 bool dispatch_single_wg(int T, int k, int n_sh) { return (int64_t)T * (k + n_sh) < DISPATCH_MANY_MIN_SLOTS; }
 
 bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                               int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                              int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
+                              int32_t* tile_expert, int32_t* tile_info, int32_t* meta, const void* x, int H,
+                              uint8_t* codes,
                               uint8_t* scales, uint8_t* a1_sf, int64_t plane, hipStream_t stream) {
   const int E = n_loc + n_sh;
   int nbits = 0;
@@ -462,7 +491,8 @@ bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, i
   const unsigned nq = (unsigned)((nblocks + per - 1) / per);
   const unsigned nf = planes ? (unsigned)((nkb + FILL_PLANES - 1) / FILL_PLANES) : 0;
   hipLaunchKernelGGL(k_dispatch_quant_mx, dim3(1 + nq + nf), dim3(DISPATCH_THREADS), 0, stream, topk_ids, T, k,
-                     n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, meta, x, nkb,
+                     n_sh, start, n_loc, bm, nbits, counts, offsets, sorted_slot, slot_row, tile_expert, tile_info, meta,
+                     x, nkb,
                      nblocks, (int)nq, codes, scales, planes ? a1_sf : nullptr, plane);
   return planes;
 }

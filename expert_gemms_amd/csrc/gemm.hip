@@ -303,11 +303,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     const int u = uu - t.ks * tiles;
     // tile -> (expert, n block, m block).  The tiles of expert e are
     // [mb0 * NB, mb1 * NB) with [mb0, mb1) its BLOCK_M blocks, so u / NB is
-    // one of e's blocks and tile_expert names e.  Scalar loads: the copies in
-    // flight are not waited for.
-    const int e = sload(p.tile_expert + u / NB);
-    const int mb0 = sload(p.offsets + e) / BM;
-    const int mcount = sload(p.offsets + e + 1) / BM - mb0;
+    // one of e's blocks, whose tile_info record names e, mb0 and mb1 - mb0.
+    // Scalar loads: the copies in flight are not waited for.
+    const i32x4 ti = sload4(p.tile_info + 4 * (u / NB));
+    const int e = ti[0], mb0 = ti[1], mcount = ti[2];
     const int local = u - mb0 * NB;
     t.e = e;
     t.nb = local / mcount;

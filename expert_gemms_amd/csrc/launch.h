@@ -33,6 +33,10 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   const int32_t* offsets;  // [E'+1], multiples of BLOCK_M
   const int32_t* tile_expert;   // [M / BLOCK_M] expert of each BLOCK_M block
+  // [M / BLOCK_M] int4 per BLOCK_M block: its expert, the expert's first
+  // block and its number of blocks (what tile_expert and offsets give, in
+  // one 16-byte record, so a tile's set-up waits out one load, not three)
+  const int32_t* tile_info;
   const float* row_scale;  // NVFP4 L1: token scale of each sorted row (1 if padding)
   const int32_t* meta;     // meta[0] = number of BLOCK_M tiles
   int kk;                  // slots per token (top_k + shared)
@@ -66,9 +70,11 @@ enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
 // kernels (same result), else one workgroup.
 constexpr int64_t DISPATCH_MANY_MIN_SLOTS = 16384;
 int64_t dispatch_scratch_ints(int64_t S, int E);
+// With tile_info, also the GemmArgs::tile_info records.
 void launch_dispatch(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                      int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                     int32_t* tile_expert, int32_t* meta, int32_t* block_counts, hipStream_t stream);
+                     int32_t* tile_expert, int32_t* tile_info, int32_t* meta, int32_t* block_counts,
+                     hipStream_t stream);
 // True when launch_dispatch runs the single-workgroup kernel.
 bool dispatch_single_wg(int T, int k, int n_sh);
 // That kernel and the MX dispatch quantisation of BF16 x [T, H] (E4M3 codes,
@@ -78,7 +84,8 @@ bool dispatch_single_wg(int T, int k, int n_sh);
 // and returns whether it did.
 bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, int start, int n_loc, int bm,
                               int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row,
-                              int32_t* tile_expert, int32_t* meta, const void* x, int H, uint8_t* codes,
+                              int32_t* tile_expert, int32_t* tile_info, int32_t* meta, const void* x, int H,
+                              uint8_t* codes,
                               uint8_t* scales, uint8_t* a1_sf, int64_t plane, hipStream_t stream);
 
 // Sum of the K parts of a split L1 GEMM (a.o, a.ksplit, a.o_split), then its
