@@ -477,6 +477,10 @@ def time_workload(args, cfg, T, flush_mb, layer, canon, min_cpu_seconds):
         "hbm_gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "mfma_frac": round(mfma_frac, 4),
+        # the step's roofline time t* = max(F / MFMA peak, B / HBM peak) and
+        # t* over the measured time (= the larger of the two fractions)
+        "t_star_ms": round(max(mfma_frac, gbs / PEAK_HBM_GBS) * ms_per_step, 4),
+        "t_star_over_t": round(max(mfma_frac, gbs / PEAK_HBM_GBS), 4),
         "step_ms": {k: round(v, 4) for k, v in per_step.items()},
         "step_ms_p10_p50_p90": [step_pct[10], step_pct[50], step_pct[90]],
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
