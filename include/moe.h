@@ -299,8 +299,11 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
  *       [block_m][32] BF16 values (a2_sf -1)
  *   o       the L2 output by slot: BF16 [S, H] when l2_rows_bf16, else
  *       float32, l2_ksplit parts of [S, H] one after another
- * The layout is for inspection (tests, debugging); it is not a stable
- * interface.  Returns MOE_OK, MOE_E_INVALID (the shape checks of
+ * The workspace also holds buffers this struct does not list (the
+ * GEMMs' per-block tile records, the many-workgroup dispatch's chunk counts,
+ * a K-split L1's float32 parts).  The layout is for inspection (tests,
+ * debugging); it is not a stable interface.  Returns MOE_OK, MOE_E_INVALID
+ * (the shape checks of
  * moe_forward) or MOE_E_WORKSPACE.  Host-only. */
 typedef struct {
   int block_m;
