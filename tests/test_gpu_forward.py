@@ -89,6 +89,18 @@ def test_forward_every_block_m(name, bm):
     compare(SMALL[name], block_m=bm)
 
 
+# Hidden 768: three 256-column N blocks in the L2 (an odd count) and six
+# 128-K stages in the L1 (24 of 32 K for BF16), fewer than some rings hold
+ODD_H = {f"{fmt}_h768": MoEConfig(f"{fmt}_h768", 70 + i, fmt, 120, 768, 384, 8, 2, routing="softmax_uniform")
+         for i, fmt in enumerate(["bf16", "mxfp8", "mxfp4", "nvfp4"])}
+
+
+@pytest.mark.parametrize("bm", [0, 64])
+@pytest.mark.parametrize("name", sorted(ODD_H))
+def test_forward_odd_hidden(name, bm):
+    compare(ODD_H[name], block_m=bm)
+
+
 @pytest.mark.parametrize("bm", [32, 128])
 @pytest.mark.parametrize("name", sorted(MULTI))
 def test_forward_several_tiles_per_workgroup(name, bm):
