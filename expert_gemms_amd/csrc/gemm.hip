@@ -540,18 +540,33 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     }
   };
 
-  // Stages rotate through NBUF LDS buffers; while stage s computes, the
-  // copies of stages s+1 .. s+NBUF-1 are in flight, those of stage
-  // s+NBUF-1 spread over stage s's K-steps into the buffer stage s-1 left.
-  // Each stage's wait + barrier sits just before its last K-step, so the
-  // next stage's first fragments are read while the last K-step's MFMAs
-  // run.  The last NBUF-1 stages of a tile issue the first stages of the
-  // workgroup's next tile (when K has at least NBUF-1 stages), so the next
-  // tile starts without a pipeline fill and its copies overlap this tile's
-  // epilogue; with no next tile, the copies re-copy the last stage into a
-  // buffer that is not read again (stage indices clamped), which keeps the
-  // copy count per stage fixed for the vmcnt bookkeeping.
-  const bool chain = nstages >= G::NBUF - 1;
+  // Stages rotate through NBUF LDS buffers.  Each stage's wait + barrier
+  // sits just before its last K-step, so the next stage's first fragments
+  // are read while the last K-step's MFMAs run; by that barrier every wave
+  // has read all of the stage's buffer.  A stage's copies go out in two
+  // windows of about half the copies each, spread over the MFMAs: the K-step
+  // window of stage s (its K-steps before the barrier) and the boundary
+  // window (the last K-step, after the barrier).  Two schedules:
+  // - late: stage s+NBUF-1 is copied into the buffer stage s-1 left, its
+  //   copies [0, LAST) in stage s's K-step window, [LAST, CPS) in its
+  //   boundary window;
+  // - early (EARLY): the buffer is refilled right after its barrier: copies
+  //   [0, PA) of stage s+NBUF go into stage s's buffer in stage s's boundary
+  //   window, the rest [PA, CPS) in stage s+1's K-step window.  Each copy
+  //   has half a stage longer to land, with the same copies per window.
+  // The 128- and 256-row MXFP8 tiles, whose weight stream waits on HBM
+  // (the M blocks of an expert share each weight line in L2, so few distinct
+  // lines are in flight), run early; the others measured faster late.  The last stages of a tile issue the first
+  // stages of the workgroup's next tile (when K has enough stages), so the
+  // next tile starts without a pipeline fill and its copies overlap this
+  // tile's epilogue; with no next tile, the copies re-copy the last stage
+  // into a buffer that is not read again (stage indices clamped), which
+  // keeps the copy count per window fixed for the vmcnt bookkeeping.
+  constexpr bool EARLY = FMT == F_MXFP8 && BM >= 128;
+  constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies in a K-step window
+  constexpr int PA = G::CPS - LAST;                          // copies in a boundary window
+  static_assert((G::NBUF - 1) * G::CPS < 64, "vmcnt holds 6 bits");
+  const bool chain = nstages >= G::NBUF - 1 + (EARLY ? 1 : 0);
   // work unit of round r: in a full round each XCD takes a contiguous run
   // (M blocks sharing a weight block meet in one L2); a partial last round
   // is dealt out across the XCDs in turn, so a small launch uses them all
@@ -594,15 +609,21 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     if (has_next) row_dma(tb);
     if (!primed) {
       // a tile the previous one could not prefetch: drain that tile's
-      // clamped re-copies, then issue stages 0 .. NBUF-2
+      // clamped re-copies, then issue stages 0 .. NBUF-2 (early: and the
+      // boundary-window copies of stage NBUF-1)
       wait_vmcnt0();
 #pragma unroll
       for (int i = 0; i + 1 < G::NBUF; ++i) {
         const int bi = cur + i < G::NBUF ? cur + i : cur + i - G::NBUF;
         issue(IC<0>{}, IC<G::CPS>{}, ta, i < nstages ? i : nstages - 1, bi);
       }
+      if constexpr (EARLY) {
+        constexpr int i = G::NBUF - 1;
+        issue(IC<0>{}, IC<PA>{}, ta, i < nstages ? i : nstages - 1, cur == 0 ? i : cur - 1);
+      }
     }
-    wait_vmcnt<(G::NBUF - 2) * G::CPS>();
+    // stage 0 has landed
+    wait_vmcnt<(G::NBUF - 2) * G::CPS + (EARLY ? PA : 0)>();
     lds_barrier();
 
 #pragma unroll
@@ -629,43 +650,54 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       constexpr int RB = decltype(rbc)::value;
       constexpr bool LASTS = decltype(lastc)::value;
       const uint8_t* st = smem + cur * G::STAGE;
-      // stage s + NBUF - 1 (of this tile, else of the next) goes into the
-      // buffer stage s - 1 left, its copies spread over stage s's K-steps
+      // K-step window: copies of stage s + NBUF - 1 (of this tile, else of
+      // the next) into the buffer stage s - 1 left; boundary window: the
+      // same stage's into the same buffer (late), or stage s + NBUF's into
+      // this stage's buffer (early)
       const int fill = cur == 0 ? G::NBUF - 1 : cur - 1;
       const int sf = s + G::NBUF - 1;
       const bool own = sf < nstages;
       const int js = own ? sf : (chain_next ? sf - nstages : nstages - 1);
-      const bool from_next = !own && chain_next;
       // copy source (a uniform branch: selects would make the tiles addressable)
       TileCtx tf = ta;
-      if (from_next) tf = tb;
+      if (!own && chain_next) tf = tb;
+      const int sfb = sf + (EARLY ? 1 : 0);
+      const bool ownb = sfb < nstages;
+      const int jsb = ownb ? sfb : (chain_next ? sfb - nstages : nstages - 1);
+      TileCtx tfb = ta;
+      if (!ownb && chain_next) tfb = tb;
       static_for<0, C::STEPS - 1>([&](auto kc) __attribute__((always_inline)) {
         constexpr int ks = decltype(kc)::value;
-        constexpr int lo = ks * G::CPS / C::STEPS, hi = (ks + 1) * G::CPS / C::STEPS;
+        constexpr int K0 = EARLY ? PA : 0;
+        constexpr int lo = K0 + ks * LAST / (C::STEPS - 1), hi = K0 + (ks + 1) * LAST / (C::STEPS - 1);
         constexpr int r0 = (RB + ks) & 1, r1 = (RB + ks + 1) & 1;
         load_frags<FMT, TM, TN, C>(st, st + G::A_STAGE, ks + 1, wm, wn, lane, af[r1], bfr[r1]);
         issue(IC<lo>{}, IC<hi>{}, tf, js, fill);
         mfmas(IC<ks>{}, IC<ks>{}, af[r0], bfr[r0], sa4, sb2);
         boundary_hint<READS, MF, hi - lo>();
       });
-      constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies of s+NBUF-1 issued so far
       constexpr int rl = (RB + C::STEPS - 1) & 1, rn = (RB + C::STEPS) & 1;
       const int nxt = cur + 1 == G::NBUF ? 0 : cur + 1;
+      // stage boundary: stage s+1 has landed (this wave's later copies may
+      // still be in flight: late, stages s+2 .. s+NBUF-2 and the K-step
+      // window's part of s+NBUF-1; early, stages s+2 .. s+NBUF-1) and every
+      // wave is done reading stage s.  Early, the last stage also needs the
+      // barrier: its boundary window writes its own buffer.
+      if constexpr (!LASTS) wait_vmcnt<EARLY ? (G::NBUF - 2) * G::CPS : (G::NBUF - 3) * G::CPS + LAST>();
+      if constexpr (!LASTS || EARLY) lds_barrier();
       if constexpr (!LASTS) {
-        // stage boundary: stage s+1 has landed (this wave's copies of
-        // stages s+2 .. s+NBUF-2 and the first part of s+NBUF-1 may still
-        // be in flight) and every wave is done reading stage s
-        wait_vmcnt<(G::NBUF - 3) * G::CPS + LAST>();
-        lds_barrier();
         const uint8_t* nx = smem + nxt * G::STAGE;
         read_scales(nx, sa4n, sb2n);
         load_frags<FMT, TM, TN, C>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
       }
-      issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
+      if constexpr (EARLY)
+        issue(IC<0>{}, IC<PA>{}, tfb, jsb, cur);
+      else
+        issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
       // with one K-step per stage, RB is the stage's parity: the half of
       // the 128-K layout stage whose B-scale byte the K-step takes
       mfmas(IC<C::STEPS - 1>{}, IC<C::STEPS == 1 ? (RB & 1) : C::STEPS - 1>{}, af[rl], bfr[rl], sa4, sb2);
-      boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + SB_N : 0), MF, G::CPS - LAST>();
+      boundary_hint<LASTS ? 0 : READS + (C::SCALED ? SA_N + SB_N : 0), MF, PA>();
       if constexpr (!LASTS) {
 #pragma unroll
         for (int tm = 0; tm < SA_N; ++tm) sa4[tm] = sa4n[tm];
