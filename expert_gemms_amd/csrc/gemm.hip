@@ -645,27 +645,17 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // One stage.  RB: register set holding the stage's first K-step
     // fragments (K-step ks uses set (RB + ks) & 1; the next stage's first
     // fragments go to set (RB + STEPS) & 1).  LASTC: the tile's last stage
-    // (no next stage to wait for or read).
-    auto stage = [&](auto rbc, auto lastc, int s) __attribute__((always_inline)) {
+    // (no next stage to wait for or read).  K-step window: copies of stage
+    // s + NBUF - 1 (tf / js: of this tile, else of the next) into the buffer
+    // stage s - 1 left; boundary window: the same stage's into the same
+    // buffer (late), or stage s + NBUF's (tfb / jsb) into this stage's
+    // buffer (early).
+    auto stage_body = [&](auto rbc, auto lastc, const TileCtx& tf, int js, const TileCtx& tfb, int jsb)
+        __attribute__((always_inline)) {
       constexpr int RB = decltype(rbc)::value;
       constexpr bool LASTS = decltype(lastc)::value;
       const uint8_t* st = smem + cur * G::STAGE;
-      // K-step window: copies of stage s + NBUF - 1 (of this tile, else of
-      // the next) into the buffer stage s - 1 left; boundary window: the
-      // same stage's into the same buffer (late), or stage s + NBUF's into
-      // this stage's buffer (early)
       const int fill = cur == 0 ? G::NBUF - 1 : cur - 1;
-      const int sf = s + G::NBUF - 1;
-      const bool own = sf < nstages;
-      const int js = own ? sf : (chain_next ? sf - nstages : nstages - 1);
-      // copy source (a uniform branch: selects would make the tiles addressable)
-      TileCtx tf = ta;
-      if (!own && chain_next) tf = tb;
-      const int sfb = sf + (EARLY ? 1 : 0);
-      const bool ownb = sfb < nstages;
-      const int jsb = ownb ? sfb : (chain_next ? sfb - nstages : nstages - 1);
-      TileCtx tfb = ta;
-      if (!ownb && chain_next) tfb = tb;
       static_for<0, C::STEPS - 1>([&](auto kc) __attribute__((always_inline)) {
         constexpr int ks = decltype(kc)::value;
         constexpr int K0 = EARLY ? PA : 0;
@@ -706,20 +696,50 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       }
       cur = nxt;
     };
+    // Stage s.  TAILC: it may copy stages past this tile's last (the next
+    // tile's, or clamped re-copies); the stages before nt copy only this
+    // tile's own stages, with no selects.
+    auto stage = [&](auto rbc, auto lastc, auto tailc, int s) __attribute__((always_inline)) {
+      const int sf = s + G::NBUF - 1;
+      const int sfb = sf + (EARLY ? 1 : 0);
+      if constexpr (decltype(tailc)::value) {
+        const bool own = sf < nstages;
+        const int js = own ? sf : (chain_next ? sf - nstages : nstages - 1);
+        // copy source (a uniform branch: selects would make the tiles addressable)
+        TileCtx tf = ta;
+        if (!own && chain_next) tf = tb;
+        const bool ownb = sfb < nstages;
+        const int jsb = ownb ? sfb : (chain_next ? sfb - nstages : nstages - 1);
+        TileCtx tfb = ta;
+        if (!ownb && chain_next) tfb = tb;
+        stage_body(rbc, lastc, tf, js, tfb, jsb);
+      } else {
+        stage_body(rbc, lastc, ta, sf, ta, sfb);
+      }
+    };
+    const int nt = nstages - (G::NBUF - 1 + (EARLY ? 1 : 0));
+    using F_ = std::false_type;
+    using T_ = std::true_type;
     if constexpr (C::STEPS % 2 == 0) {
-      for (int s = 0; s + 1 < nstages; ++s) stage(IC<0>{}, std::false_type{}, s);
-      stage(IC<0>{}, std::true_type{}, nstages - 1);
+      int s = 0;
+      for (; s < nt && s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, F_{}, s);
+      for (; s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, T_{}, s);
+      stage(IC<0>{}, T_{}, T_{}, nstages - 1);
     } else {
       int s = 0;
+      for (; s + 1 < nt && s + 2 < nstages; s += 2) {
+        stage(IC<0>{}, F_{}, F_{}, s);
+        stage(IC<1>{}, F_{}, F_{}, s + 1);
+      }
       for (; s + 2 < nstages; s += 2) {
-        stage(IC<0>{}, std::false_type{}, s);
-        stage(IC<1>{}, std::false_type{}, s + 1);
+        stage(IC<0>{}, F_{}, T_{}, s);
+        stage(IC<1>{}, F_{}, T_{}, s + 1);
       }
       if (s + 1 < nstages) {
-        stage(IC<0>{}, std::false_type{}, s);
-        stage(IC<1>{}, std::true_type{}, s + 1);
+        stage(IC<0>{}, F_{}, T_{}, s);
+        stage(IC<1>{}, T_{}, T_{}, s + 1);
       } else {
-        stage(IC<0>{}, std::true_type{}, s);
+        stage(IC<0>{}, T_{}, T_{}, s);
       }
     }
     primed = chain_next;
