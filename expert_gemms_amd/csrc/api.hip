@@ -303,6 +303,14 @@ int check_shape(int fmt, int num_tokens, int hidden, int inter, int top_k, int n
     return MOE_E_INVALID;
   if ((int64_t)num_tokens * (top_k + num_shared) > (int64_t)1 << 30) return MOE_E_INVALID;
   if (block_m != 0 && block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return MOE_E_INVALID;
+  // the GEMMs copy each expert's weights and the quantised x through buffer
+  // resources with 32-bit offsets: both stay below 4 GiB (a 1 MiB margin for
+  // the offsets within a row).  w13 holds 2 I H elements per expert, of 2
+  // (BF16), 1 (MXFP8) or 1/2 bytes; x's codes are 1 byte (MX) or 1/2 (NVFP4).
+  const int64_t lim = ((int64_t)1 << 32) - ((int64_t)1 << 20);
+  const int64_t w13_bytes = (int64_t)inter * hidden * (fmt == MOE_FMT_BF16 ? 4 : fmt == MOE_FMT_MXFP8 ? 2 : 1);
+  const int64_t x_bytes = (int64_t)num_tokens * hidden / (fmt == MOE_FMT_NVFP4 ? 2 : 1);
+  if (w13_bytes >= lim || (fmt != MOE_FMT_BF16 && x_bytes >= lim)) return MOE_E_INVALID;
   return MOE_OK;
 }
 

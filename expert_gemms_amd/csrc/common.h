@@ -221,4 +221,19 @@ __device__ __forceinline__ void g2lds16_nt(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 2);
 }
 
+// A raw buffer resource over the bytes from `base` on (no range limit, no
+// stride: the gfx9 dword-3 word), for copies addressed by 32-bit offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy: lane l's 16 bytes at byte voff (per lane) +
+// soff (uniform) of the buffer land at `lds_base + 16 * l`, the same as
+// g2lds16, with the offset sum done by the load itself rather than by 64-bit
+// address arithmetic per copy.  NT: the non-temporal cache policy.
+template <bool NT = false>
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, NT ? 2 : 0);
+}
+
 }  // namespace moe

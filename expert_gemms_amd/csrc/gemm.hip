@@ -282,6 +282,16 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
 
+  // A rows and weight fragments are copied through buffer resources with
+  // 32-bit offsets (a per-lane offset and a per-stage uniform one), so a copy
+  // needs no 64-bit address arithmetic.  A rows gathered from x (L1, K-split
+  // L1) are addressed from x itself; the L2's rows and the BF16 stage-blocked
+  // rows from the tile's first row.  The host keeps x and each expert's
+  // weights below 4 GiB.
+  constexpr bool BLOCKED = FMT == F_BF16;               // A rows stage-blocked, in sorted order
+  constexpr bool TILE_A = BLOCKED || LAYER == 2;        // A resource per tile
+  const __amdgpu_buffer_rsrc_t ra_x = buf_rsrc(p.a);
+
   // One tile: an expert, a 256-column block and a BLOCK_M-row block, with the
   // per-lane source offsets of its A rows.
   struct TileCtx {
@@ -289,9 +299,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     int s0;                 // first K stage of the work unit
     int ks;                 // its K split
     int par;                // its row buffer
-    int64_t a_off[G::A_INSTR];
-    const uint8_t* wexp;
-    const uint8_t* wbase;   // the tile's N block of the weights (layout stage 0)
+    uint32_t a_off[G::A_INSTR];
+    __amdgpu_buffer_rsrc_t ra;   // TILE_A: the tile's A rows
+    __amdgpu_buffer_rsrc_t rw;   // the tile's N block of the weights (layout stage 0)
     const uint8_t* wsf;
     const uint8_t* asf;     // MX: the wave's A-scale plane at the tile's first row (stage 0)
     const uint8_t* bsf;     // MX: the wave's B-scale column blocks (layout stage 0)
@@ -316,8 +326,6 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // (rows wrap modulo BM when a wave has more lanes than rows).  L1: the
     // wave's A_WROWS contiguous rows' slots come in by scalar loads and each
     // lane picks its rows' token.
-    // BF16: A rows are stage-blocked and already in sorted order
-    constexpr bool BLOCKED = FMT == F_BF16;
     int sv[G::A_WROWS];
     if constexpr (LAYER != 2 && !BLOCKED) {
       const int32_t* base = p.sorted_slot + t.m0 + (w * G::A_WROWS) % BM;
@@ -338,27 +346,29 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     for (int i = 0; i < G::A_INSTR; ++i) {
       const int rl = (w * G::A_INSTR + i) * G::A_RPI + lane / G::A_CPR;
       const int r = rl % BM;
-      int64_t row;
+      const uint32_t chunk = (uint32_t)swz<C::A_ROW>(rl, lane % G::A_CPR) << 4;
       if constexpr (BLOCKED) {
-        // the tile's block of the [M / BM][K / 32][BM][64 B] layout, row r
-        t.a_off[i] = ((int64_t)(t.m0 / BM) * (p.K / 32) * BM + r) * 64 + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
-        continue;
+        // row r of the tile's block of the [M / BM][K / 32][BM][64 B] layout
+        t.a_off[i] = (uint32_t)r * 64 + chunk;
       } else if constexpr (LAYER != 2) {
         int sl = sv[i * G::A_RPI];
 #pragma unroll
         for (int k = 1; k < G::A_RPI; ++k)
           if (lane / G::A_CPR == k) sl = sv[i * G::A_RPI + k];
-        row = sl >= 0 ? sl / p.kk : 0;
+        t.a_off[i] = (uint32_t)(sl >= 0 ? sl / p.kk : 0) * (uint32_t)p.a_ld + chunk;
       } else {
-        row = t.m0 + r;
+        t.a_off[i] = (uint32_t)r * (uint32_t)p.a_ld + chunk;
       }
-      t.a_off[i] = row * p.a_ld + (swz<C::A_ROW>(rl, lane % G::A_CPR) << 4);
     }
-    t.wexp = p.w + (int64_t)e * p.w_expert_bytes;
+    if constexpr (BLOCKED)
+      t.ra = buf_rsrc(p.a + (int64_t)(t.m0 / BM) * (p.K / 32) * BM * 64);
+    else if constexpr (LAYER == 2)
+      t.ra = buf_rsrc(p.a + (int64_t)t.m0 * p.a_ld);
     {
       constexpr int LSK = C::KSTAGE / C::STEPS * C::KS_PER_L;   // K per layout stage
-      t.wbase = t.wexp + (FMT == F_BF16 ? (int64_t)t.nb * (p.K / LSK) * 8 * (C::KS_PER_L * C::FRAG)
-                                        : (int64_t)t.nb * 8 * (C::KS_PER_L * C::FRAG));
+      t.rw = buf_rsrc(p.w + (int64_t)e * p.w_expert_bytes +
+                      (FMT == F_BF16 ? (int64_t)t.nb * (p.K / LSK) * 8 * (C::KS_PER_L * C::FRAG)
+                                     : (int64_t)t.nb * 8 * (C::KS_PER_L * C::FRAG)));
     }
     t.wsf = C::SCALED ? p.w_sf + (int64_t)e * p.w_sf_expert_bytes : nullptr;
     if constexpr (C::SCALED && !C::NV) {
@@ -374,13 +384,13 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     constexpr int c = decltype(ci)::value;
     constexpr int SC = G::A_INSTR + G::B_INSTR;   // first scale copy
     if constexpr (c < G::A_INSTR) {
-      constexpr int64_t SSTRIDE = FMT == F_BF16 ? (int64_t)BM * C::A_ROW : C::A_ROW;   // bytes per stage of a row
-      g2lds16(p.a + t.a_off[c] + (int64_t)(t.s0 + s) * SSTRIDE, st + (w * G::A_INSTR + c) * 1024);
+      constexpr uint32_t SSTRIDE = FMT == F_BF16 ? BM * C::A_ROW : C::A_ROW;   // bytes per stage of a row
+      buf2lds16(TILE_A ? t.ra : ra_x, t.a_off[c], (uint32_t)(t.s0 + s) * SSTRIDE, st + (w * G::A_INSTR + c) * 1024);
     } else if constexpr (c < SC) {
       // weight fragments: LDS [32-row block][K-step of the stage][FRAG];
       // global BF16 [N block][layout stage][32-row block of 8][KS_PER_L
       // K-steps][FRAG], others [layout stage][32-row block][KS_PER_L][FRAG]
-      // the tile's weight base (t.wbase), a term per stage (layout stage
+      // the tile's weight resource (t.rw), a term per stage (layout stage
       // S / R of the tile's N block, K-step (S % R) * STEPS within it) and a
       // term per copy (32-row block nf, K-step ksl of the stage, 1 KiB piece)
       const int q = w * G::B_INSTR + (c - G::A_INSTR);
@@ -388,19 +398,16 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const int ksl = piece / (C::FRAG / 1024), sub = piece % (C::FRAG / 1024);
       constexpr unsigned R = C::KS_PER_L / C::STEPS;   // kernel stages per layout stage
       const unsigned S = (unsigned)(t.s0 + s);
-      const int64_t lstride = FMT == F_BF16 ? (int64_t)8 * C::KS_PER_L * C::FRAG
-                                            : (int64_t)(p.N / 32) * (C::KS_PER_L * C::FRAG);
-      const int64_t sterm = (int64_t)(S / R) * lstride + (int64_t)((S % R) * (C::STEPS * C::FRAG));
-      const int cterm = nf * (C::KS_PER_L * C::FRAG) + ksl * C::FRAG + sub * 1024;
+      const uint32_t lstride = FMT == F_BF16 ? 8u * C::KS_PER_L * C::FRAG
+                                             : (uint32_t)(p.N / 32) * (C::KS_PER_L * C::FRAG);
+      const uint32_t sterm = (S / R) * lstride + (S % R) * (C::STEPS * C::FRAG);
+      const uint32_t cterm = nf * (C::KS_PER_L * C::FRAG) + ksl * C::FRAG + sub * 1024;
       // 32-row tiles (the BLOCK_M of decode-sized batches, where an expert
       // rarely has more than one M block) stream their weights: each line is
       // read by one workgroup once, so it is copied non-temporally and does
       // not displace lines that are still to be read.  Taller tiles share
       // weight blocks between an expert's M blocks and keep them cached.
-      if constexpr (BM <= 32)
-        g2lds16_nt(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
-      else
-        g2lds16(t.wbase + sterm + cterm + lane * 16, st + G::A_STAGE + q * 1024);
+      buf2lds16<(BM <= 32)>(t.rw, cterm + (uint32_t)lane * 16, sterm, st + G::A_STAGE + q * 1024);
     } else if constexpr (!C::NV && c == SC) {
       // A scales: K block w % (blocks per stage) of this stage, the plane's
       // bytes of rows m0 .. m0+255 (rows past the tile are not read)

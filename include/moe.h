@@ -242,8 +242,11 @@ int moe_dispatch(int num_tokens, int top_k, int num_shared, int expert_start,
  *   out           BF16 [T, H], fully overwritten            (device)
  *   workspace     >= moe_workspace_bytes(fmt, T, ..., block_m) bytes (device)
  * hidden, inter multiples of 128; 1 <= top_k; num_local_experts >= 1;
- * num_tokens >= 0 (0 enqueues nothing).  Asynchronous; calls on one stream
- * may share a workspace, concurrent calls need their own. */
+ * num_tokens >= 0 (0 enqueues nothing); one expert's w13 codes (2 * inter *
+ * hidden elements) and, for the block-scaled formats, x's codes
+ * (num_tokens * hidden elements) each below 4 GiB, which the GEMMs address
+ * with 32-bit offsets.  MOE_E_INVALID otherwise.  Asynchronous; calls on one
+ * stream may share a workspace, concurrent calls need their own. */
 int moe_forward(moe_format_t fmt, int num_tokens, int hidden, int inter, int top_k,
                 int expert_start, int num_local_experts, int num_shared, int block_m,
                 const moe_activation_t* act, const moe_options_t* opts,

@@ -109,6 +109,8 @@ def _fwd(**kw):
     dict(opts=_lib.Options(0x10000, 1e-6, 0), H=16640),   # norm row does not fit LDS
     dict(opts=_lib.Options(None, 0.0, 1)),       # weight on input with top_k = 2
     dict(opts=_lib.Options(None, 0.0, 1), k=1, nsh=1),     # ... or with a shared expert
+    dict(H=16384, I=65536),                      # one expert's w13 reaches 4 GiB (32-bit copy offsets)
+    dict(fmt=1, w13sf=_Fake(), w2sf=_Fake(), T=1 << 19, H=8192),   # x's MX codes reach 4 GiB
 ])
 def test_forward_rejects_invalid_arguments(kw):
     assert _fwd(**kw) == _lib.E_INVALID
