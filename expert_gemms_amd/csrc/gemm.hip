@@ -657,12 +657,15 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // stage s - 1 left; boundary window: the same stage's into the same
     // buffer (late), or stage s + NBUF's (tfb / jsb) into this stage's
     // buffer (early).
-    auto stage_body = [&](auto rbc, auto lastc, const TileCtx& tf, int js, const TileCtx& tfb, int jsb)
+    // CURC: the stage's buffer when known at compile time (else -1: cur).
+    auto stage_body = [&](auto rbc, auto lastc, auto curc, const TileCtx& tf, int js, const TileCtx& tfb, int jsb)
         __attribute__((always_inline)) {
       constexpr int RB = decltype(rbc)::value;
       constexpr bool LASTS = decltype(lastc)::value;
-      const uint8_t* st = smem + cur * G::STAGE;
-      const int fill = cur == 0 ? G::NBUF - 1 : cur - 1;
+      constexpr int CURC = decltype(curc)::value;
+      const int cb = CURC >= 0 ? CURC : cur;
+      const uint8_t* st = smem + cb * G::STAGE;
+      const int fill = CURC >= 0 ? (CURC == 0 ? G::NBUF - 1 : CURC - 1) : (cur == 0 ? G::NBUF - 1 : cur - 1);
       static_for<0, C::STEPS - 1>([&](auto kc) __attribute__((always_inline)) {
         constexpr int ks = decltype(kc)::value;
         constexpr int K0 = EARLY ? PA : 0;
@@ -674,7 +677,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         boundary_hint<READS, MF, hi - lo>();
       });
       constexpr int rl = (RB + C::STEPS - 1) & 1, rn = (RB + C::STEPS) & 1;
-      const int nxt = cur + 1 == G::NBUF ? 0 : cur + 1;
+      const int nxt = CURC >= 0 ? (CURC + 1) % G::NBUF : (cur + 1 == G::NBUF ? 0 : cur + 1);
       // stage boundary: stage s+1 has landed (this wave's later copies may
       // still be in flight: late, stages s+2 .. s+NBUF-2 and the K-step
       // window's part of s+NBUF-1; early, stages s+2 .. s+NBUF-1) and every
@@ -688,7 +691,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         load_frags<FMT, TM, TN, C>(nx, nx + G::A_STAGE, 0, wm, wn, lane, af[rn], bfr[rn]);
       }
       if constexpr (EARLY)
-        issue(IC<0>{}, IC<PA>{}, tfb, jsb, cur);
+        issue(IC<0>{}, IC<PA>{}, tfb, jsb, cb);
       else
         issue(IC<LAST>{}, IC<G::CPS>{}, tf, js, fill);
       // with one K-step per stage, RB is the stage's parity: the half of
@@ -706,7 +709,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     // Stage s.  TAILC: it may copy stages past this tile's last (the next
     // tile's, or clamped re-copies); the stages before nt copy only this
     // tile's own stages, with no selects.
-    auto stage = [&](auto rbc, auto lastc, auto tailc, int s) __attribute__((always_inline)) {
+    auto stage = [&](auto rbc, auto lastc, auto tailc, int s, auto curc) __attribute__((always_inline)) {
       const int sf = s + G::NBUF - 1;
       const int sfb = sf + (EARLY ? 1 : 0);
       if constexpr (decltype(tailc)::value) {
@@ -719,34 +722,43 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         const int jsb = ownb ? sfb : (chain_next ? sfb - nstages : nstages - 1);
         TileCtx tfb = ta;
         if (!ownb && chain_next) tfb = tb;
-        stage_body(rbc, lastc, tf, js, tfb, jsb);
+        stage_body(rbc, lastc, curc, tf, js, tfb, jsb);
       } else {
-        stage_body(rbc, lastc, ta, sf, ta, sfb);
+        stage_body(rbc, lastc, curc, ta, sf, ta, sfb);
       }
     };
     const int nt = nstages - (G::NBUF - 1 + (EARLY ? 1 : 0));
     using F_ = std::false_type;
     using T_ = std::true_type;
+    using RT_ = IC<-1>;   // buffer index at run time
     if constexpr (C::STEPS % 2 == 0) {
+      // own-tile stages: until the ring is back at buffer 0, then in groups
+      // of NBUF whose buffers are compile-time constants (no ring-index or
+      // LDS-address arithmetic per stage), then the rest
       int s = 0;
-      for (; s < nt && s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, F_{}, s);
-      for (; s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, T_{}, s);
-      stage(IC<0>{}, T_{}, T_{}, nstages - 1);
+      for (; s < nt && cur != 0; ++s) stage(IC<0>{}, F_{}, F_{}, s, RT_{});
+      for (; s + G::NBUF <= nt; s += G::NBUF)
+        static_for<0, G::NBUF>([&](auto jc) __attribute__((always_inline)) {
+          stage(IC<0>{}, F_{}, F_{}, s + decltype(jc)::value, jc);
+        });
+      for (; s < nt && s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, F_{}, s, RT_{});
+      for (; s + 1 < nstages; ++s) stage(IC<0>{}, F_{}, T_{}, s, RT_{});
+      stage(IC<0>{}, T_{}, T_{}, nstages - 1, RT_{});
     } else {
       int s = 0;
       for (; s + 1 < nt && s + 2 < nstages; s += 2) {
-        stage(IC<0>{}, F_{}, F_{}, s);
-        stage(IC<1>{}, F_{}, F_{}, s + 1);
+        stage(IC<0>{}, F_{}, F_{}, s, RT_{});
+        stage(IC<1>{}, F_{}, F_{}, s + 1, RT_{});
       }
       for (; s + 2 < nstages; s += 2) {
-        stage(IC<0>{}, F_{}, T_{}, s);
-        stage(IC<1>{}, F_{}, T_{}, s + 1);
+        stage(IC<0>{}, F_{}, T_{}, s, RT_{});
+        stage(IC<1>{}, F_{}, T_{}, s + 1, RT_{});
       }
       if (s + 1 < nstages) {
-        stage(IC<0>{}, F_{}, T_{}, s);
-        stage(IC<1>{}, T_{}, T_{}, s + 1);
+        stage(IC<0>{}, F_{}, T_{}, s, RT_{});
+        stage(IC<1>{}, T_{}, T_{}, s + 1, RT_{});
       } else {
-        stage(IC<0>{}, T_{}, T_{}, s);
+        stage(IC<0>{}, T_{}, T_{}, s, RT_{});
       }
     }
     primed = chain_next;
