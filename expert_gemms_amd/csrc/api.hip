@@ -105,13 +105,18 @@ struct Workspace {
   uint8_t* a2_sf;     // L2 input block scales, planes of sorted rows
   float* p1;          // K parts of a split L1 GEMM, float32 [ksplit1, S, 2I]
   float* o;           // L2 output rows per slot
+  float* o_tail;      // split-tail L2: the tail tiles' K parts (TAIL_UNITS units)
   uint16_t* xw;       // BF16 input rows scaled by their routing weight
   uint16_t* xs;       // BF16: sorted x rows, stage-blocked (the L1 A operand)
   size_t bytes;
 };
 
+// Work units a split-tail L2's parts buffer holds (one round of the 256-CU
+// grid); the GEMM splits no more of its tail than fit.
+constexpr int TAIL_UNITS = 256;
+
 Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t n_sh, int64_t k, int64_t bm,
-               int64_t ksplit, int64_t ksplit1, uint8_t* base) {
+               int64_t ksplit, int64_t ksplit1, int64_t tail_kmax, uint8_t* base) {
   const int64_t E = n_loc + n_sh, S = T * (k + n_sh), M = S + E * (bm - 1);
   Workspace w;
   size_t off = 0;
@@ -151,6 +156,7 @@ Workspace plan(int fmt, int64_t T, int64_t H, int64_t I, int64_t n_loc, int64_t 
     w.xs = (uint16_t*)take(Mb * H * 2);
   }
   w.o = (float*)take(S * H * 4 * ksplit);
+  w.o_tail = tail_kmax > 1 ? (float*)take((int64_t)TAIL_UNITS * bm * GEMM_BN * 4) : nullptr;
   w.p1 = ksplit1 > 1 ? (float*)take(S * 2 * I * 4 * ksplit1) : nullptr;
   w.xw = (uint16_t*)take(T * H * 2);
   w.bytes = off;
@@ -257,6 +263,21 @@ int l2_ksplit(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int
   return best;
 }
 
+// BF16 L2s (float32 rows) with at least as many tiles as the rule's CUs
+// split only the persistent grid's partial last round (TailSplit; the
+// largest kmax of 4, 2 that divides the stage count) instead of every tile:
+// whole tiles keep one part and one epilogue.  0: no split tail.
+int l2_tail_kmax(int fmt, int64_t T, int64_t H, int64_t I, int n_loc, int n_sh, int k, int cus) {
+  if (fmt != MOE_FMT_BF16 || T <= 0 || cus <= 0) return 0;
+  const int bm = block_m_rule((int)T, n_loc, n_sh, k, fmt);
+  const double mtiles = n_loc * expected_padded((double)T * k / n_loc, bm) / bm +
+                        n_sh * (double)((T + bm - 1) / bm);
+  if (mtiles * (double)(H / GEMM_BN) < cus) return 0;
+  for (int km = 4; km >= 2; km >>= 1)
+    if ((I / 32) % km == 0) return km;
+  return 0;
+}
+
 // K splits of the L1 GEMM, for launches with few tiles (decode batches):
 // when the tiles leave work slots idle (two per CU for the small tiles such
 // launches use), each tile's K is cut into ks parts that run as separate work
@@ -318,23 +339,28 @@ int check_shape(int fmt, int num_tokens, int hidden, int inter, int top_k, int n
 // the rule's BLOCK_M when block_m is 0; the K splits the rules pick, each
 // dropped (L1 first) while the workspace cannot hold its float32 parts.
 struct Resolved {
-  int bm, ks, ks1;
+  int bm, ks, ks1, tail;   // tail: the L2's split-tail kmax (0: none)
   Workspace w;
 };
 int resolve(int fmt, int num_tokens, int hidden, int inter, int top_k, int num_local_experts, int num_shared,
             int block_m, size_t workspace_bytes, uint8_t* base, Resolved* r) {
   const int bm = block_m ? block_m : block_m_rule(num_tokens, num_local_experts, num_shared, top_k, fmt);
   const int64_t T = num_tokens, H = hidden, I = inter;
-  int ks = l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  int tail = l2_tail_kmax(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  int ks = tail ? 1 : l2_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
   int ks1 = l1_ksplit(fmt, T, H, I, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  auto need = [&]() { return plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, nullptr).bytes; };
+  auto need = [&]() {
+    return plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, tail, nullptr).bytes;
+  };
   if (need() > workspace_bytes) ks1 = 1;
   if (need() > workspace_bytes) ks = 1;
+  if (need() > workspace_bytes) tail = 0;
   if (need() > workspace_bytes) return MOE_E_WORKSPACE;
   r->bm = bm;
   r->ks = ks;
   r->ks1 = ks1;
-  r->w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, base);
+  r->tail = tail;
+  r->w = plan(fmt, T, H, I, num_local_experts, num_shared, top_k, bm, ks, ks1, tail, base);
   return MOE_OK;
 }
 
@@ -375,9 +401,12 @@ size_t moe_workspace_bytes(moe_format_t fmt, int max_tokens, int hidden, int int
     return 0;
   if (block_m == 0) block_m = 256;
   if (block_m != 32 && block_m != 64 && block_m != 128 && block_m != 256) return 0;
-  const int ks = l2_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  const int tail = l2_tail_kmax(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
+  const int ks =
+      tail ? 1 : l2_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
   const int ks1 = l1_ksplit(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, SPLIT_RULE_CUS);
-  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, ks, ks1, nullptr).bytes;
+  return plan(fmt, max_tokens, hidden, inter, num_local_experts, num_shared, top_k, block_m, ks, ks1, tail, nullptr)
+      .bytes;
 }
 
 int moe_transform_weights(moe_format_t fmt, int num_experts, int hidden, int inter, const void* w13,
@@ -565,7 +594,7 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   int st = device_info(&d);
   if (st != MOE_OK) return st;
   if (noalloc && (st = scratch_of(d, &workspace)) != MOE_OK) return st;
-  rs.w = plan(fmt, num_tokens, hidden, inter, num_local_experts, num_shared, top_k, rs.bm, rs.ks, rs.ks1,
+  rs.w = plan(fmt, num_tokens, hidden, inter, num_local_experts, num_shared, top_k, rs.bm, rs.ks, rs.ks1, rs.tail,
               (uint8_t*)workspace);
   const int bm = rs.bm, ks = rs.ks, ks1 = rs.ks1;
   const Workspace& w = rs.w;
@@ -687,6 +716,9 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
   g2.ksplit = ks;
   g2.o_bf16 = scaled && ks == 1;
   g2.o_split = (int64_t)T * kk * H;
+  g2.o_tail = w.o_tail;
+  g2.tail_kmax = rs.tail;
+  g2.tail_units = TAIL_UNITS;
   mark(2 * MOE_STEP_L2);
   e = launch_gemm(fmt, 2, bm, g2, grid, s);
   if (e != hipSuccess) return hip_status(e);
@@ -694,9 +726,11 @@ int forward_impl(moe_format_t fmt, int num_tokens, int hidden, int inter, int to
 
   // a7: weighted combine
   mark(2 * MOE_STEP_COMBINE);
-  launch_combine(w.o, g2.o_bf16, ks, (int64_t)T * kk * H, w.slot_row, o.apply_router_weight_on_input ? nullptr : topk_weights,
-                 num_tokens, top_k, (int)kk, (int)H, o.post_expert_norm_gamma, o.post_expert_norm_eps,
-                 (uint16_t*)out, s);
+  const CombineTail tl = {rs.tail > 1 ? w.o_tail : nullptr, w.tile_info, w.meta, bm,
+                          gemm_workgroups(fmt, bm, grid), rs.tail, TAIL_UNITS, (int)(I / 32)};
+  launch_combine(w.o, g2.o_bf16, ks, (int64_t)T * kk * H, w.slot_row,
+                 o.apply_router_weight_on_input ? nullptr : topk_weights, num_tokens, top_k, (int)kk, (int)H,
+                 o.post_expert_norm_gamma, o.post_expert_norm_eps, tl, (uint16_t*)out, s);
   mark(2 * MOE_STEP_COMBINE + 1);
   return hip_status(hipGetLastError());
 }

@@ -32,21 +32,48 @@ __device__ __forceinline__ f32x4 slot_cols(const float* __restrict__ o, int nspl
   }
 }
 
+// Columns h .. h+3 of slot s after an L2 with a split tail (TailSplit ts):
+// the slot's row in the tile that computed those columns (BLOCK_M block of
+// its sorted row m, 256-column block of h, numbered as the GEMM numbers its
+// tiles) is a whole tile's row in o, or a tail tile's parts in o_tail, added
+// in part order.  A dropped slot (m < 0) gives zeros.
+__device__ __forceinline__ f32x4 slot_cols_tail(const float* __restrict__ o, const CombineTail& tl, TailSplit ts,
+                                                const int32_t* __restrict__ slot_row, int64_t s, int H, int h) {
+  const int m = slot_row[s];
+  if (m < 0) return (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  const int mb = m / tl.bm;
+  const int4 ti = *(const int4*)(tl.tile_info + 4 * mb);   // expert, its first block, its block count
+  const int u = ti.y * (H / GEMM_BN) + (h / GEMM_BN) * ti.z + (mb - ti.y);
+  if (u < ts.full) return __builtin_nontemporal_load((const f32x4*)(o + s * H + h));
+  const float* p = tl.o_tail + ((int64_t)(u - ts.full) * ts.kt * tl.bm + m % tl.bm) * GEMM_BN + h % GEMM_BN;
+  f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+  for (int q = 1; q < ts.kt; ++q) v += __builtin_nontemporal_load((const f32x4*)(p + (int64_t)q * tl.bm * GEMM_BN));
+  return v;
+}
+
 // Weighted sum of token t's slot rows at columns h .. h+3, in slot order.
 // The rows are loaded 8 slots at a time before any is added, so a thread
 // keeps 8 loads in flight; a dropped slot's row (never written) is loaded
-// but not added.
-template <bool O16>
+// but not added.  TL: float32 rows of an L2 with a split tail.
+template <bool O16, bool TL = false>
 __device__ __forceinline__ f32x4 token_sum(const float* __restrict__ o, int nsplit, int64_t o_split,
                                            const int32_t* __restrict__ slot_row,
-                                           const float* __restrict__ topk_w, int t, int k, int kk, int H, int h) {
+                                           const float* __restrict__ topk_w, int t, int k, int kk, int H, int h,
+                                           const CombineTail& tl = CombineTail{}) {
   const int64_t s0 = (int64_t)t * kk;
+  TailSplit ts = {0, 0, 1};
+  if constexpr (TL) ts = tail_split(tl.meta[0] * (H / GEMM_BN), tl.nw, tl.kmax, tl.cap, tl.nst);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int j0 = 0; j0 < kk; j0 += 8) {
     f32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (j0 + i < kk) v[i] = slot_cols<O16>(o, nsplit, o_split, s0 + j0 + i, H, h);
+      if (j0 + i < kk) {
+        if constexpr (TL)
+          v[i] = slot_cols_tail(o, tl, ts, slot_row, s0 + j0 + i, H, h);
+        else
+          v[i] = slot_cols<O16>(o, nsplit, o_split, s0 + j0 + i, H, h);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -112,15 +139,15 @@ __global__ void __launch_bounds__(1024) k_combine16(const uint16_t* __restrict__
 }
 
 // Workgroup (t, c): token t, columns [1024 c, 1024 c + 1024), 4 per thread.
-template <bool O16>
+template <bool O16, bool TL>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, int nsplit, int64_t o_split,
                                                  const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ topk_w, int k, int kk, int H,
-                                                 uint16_t* __restrict__ out) {
+                                                 CombineTail tl, uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
   const int h = blockIdx.y * 1024 + threadIdx.x * 4;
   if (h >= H) return;
-  const f32x4 acc = token_sum<O16>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
+  const f32x4 acc = token_sum<O16, TL>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h, tl);
   uint2 packed;
   packed.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
   packed.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
@@ -130,18 +157,18 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ o, in
 // With the post-expert RMSNorm: one workgroup per token keeps the float32 row
 // in LDS, sums its squares, then writes y / sqrt(mean(y^2) + eps) * gamma.
 // The weighting matches k_combine element for element.
-template <bool O16>
+template <bool O16, bool TL>
 __global__ void __launch_bounds__(256) k_combine_norm(const float* __restrict__ o, int nsplit, int64_t o_split,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ topk_w, int k, int kk, int H,
-                                                      const float* __restrict__ gamma, float eps,
+                                                      const float* __restrict__ gamma, float eps, CombineTail tl,
                                                       uint16_t* __restrict__ out) {
   extern __shared__ f32x4 rowv[];   // H / 4
   __shared__ float red[4];
   const int t = blockIdx.x;
   float ss = 0.0f;
   for (int h = threadIdx.x * 4; h < H; h += 1024) {
-    const f32x4 acc = token_sum<O16>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h);
+    const f32x4 acc = token_sum<O16, TL>(o, nsplit, o_split, slot_row, topk_w, t, k, kk, H, h, tl);
     rowv[h >> 2] = acc;
     ss += acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
   }
@@ -178,24 +205,30 @@ __global__ void __launch_bounds__(256) k_scale_rows(const uint16_t* __restrict__
 }
 
 void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, const int32_t* slot_row,
-                    const float* topk_w, int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out,
-                    hipStream_t stream) {
+                    const float* topk_w, int T, int k, int kk, int H, const float* gamma, float eps,
+                    const CombineTail& tl, uint16_t* out, hipStream_t stream) {
   const dim3 grid(T, (H + 1023) / 1024);
+  const bool tail = !o_bf16 && tl.o_tail;
   if (gamma && o_bf16)
-    hipLaunchKernelGGL(k_combine_norm<true>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split, slot_row,
-                       topk_w, k, kk, H, gamma, eps, out);
+    hipLaunchKernelGGL((k_combine_norm<true, false>), dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
+                       slot_row, topk_w, k, kk, H, gamma, eps, tl, out);
+  else if (gamma && tail)
+    hipLaunchKernelGGL((k_combine_norm<false, true>), dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
+                       slot_row, topk_w, k, kk, H, gamma, eps, tl, out);
   else if (gamma)
-    hipLaunchKernelGGL(k_combine_norm<false>, dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
-                       slot_row, topk_w, k, kk, H, gamma, eps, out);
+    hipLaunchKernelGGL((k_combine_norm<false, false>), dim3(T), dim3(256), (size_t)H * 4, stream, o, nsplit, o_split,
+                       slot_row, topk_w, k, kk, H, gamma, eps, tl, out);
   else if (o_bf16) {
     // H / 8 threads (a multiple of 16, as H is of 128), at most 1024
     const int threads = H / 8 <= 1024 ? H / 8 : 1024;
     hipLaunchKernelGGL(k_combine16, dim3(T, (H / 8 + threads - 1) / threads), dim3(threads), 0, stream,
                        (const uint16_t*)o, slot_row, topk_w, k, kk, H, out);
-  }
+  } else if (tail)
+    hipLaunchKernelGGL((k_combine<false, true>), grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k,
+                       kk, H, tl, out);
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k, kk, H,
-                       out);
+    hipLaunchKernelGGL((k_combine<false, false>), grid, dim3(256), 0, stream, o, nsplit, o_split, slot_row, topk_w, k,
+                       kk, H, tl, out);
 }
 
 void launch_scale_rows(const uint16_t* x, const float* w, int T, int H, uint16_t* xw, hipStream_t stream) {

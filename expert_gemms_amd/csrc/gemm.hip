@@ -274,11 +274,22 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
             l32 = lane & 31;
   const int wm = w / G::WN, wn = w % G::WN;
   const int NB = p.N / GEMM_BN;
-  // L2 may split K: work unit u covers tile u % tiles and stages
-  // [ks * nstages, (ks + 1) * nstages) of K, ks = u / tiles
-  const int nstages = p.K / C::KSTAGE / p.ksplit;
+  // Work units: the first `full` tiles whole, then `tail` tiles as kt K
+  // parts each (unit full + ks * tail + i: part ks of tile full + i, stages
+  // [ks * nst / kt, (ks + 1) * nst / kt)).  A uniform K split (ksplit) has
+  // full = 0, tail = tiles; an L2 with a split tail splits only the
+  // persistent grid's partial last round (tail_split).
+  const int nst = p.K / C::KSTAGE;   // stages of a whole tile
   const int tiles = p.meta[0] * NB;
-  const int total = tiles * p.ksplit;
+  constexpr bool TAILBUF = LAYER == 2 && FMT == F_BF16;   // float32 rows: a split tail is possible
+  int full = 0, tail = tiles, kt = p.ksplit;
+  if (TAILBUF && p.tail_kmax > 1) {
+    const TailSplit ts = tail_split(tiles, (int)gridDim.x, p.tail_kmax, p.tail_units, nst);
+    full = ts.full;
+    tail = ts.tail;
+    kt = ts.kt;
+  }
+  const int total = full + tail * kt;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
 
@@ -299,6 +310,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
     int s0;                 // first K stage of the work unit
     int ks;                 // its K split
     int par;                // its row buffer
+    int ns;                 // its K stages
+    int tidx;               // split tail: its tile's index in the tail, else -1
     uint32_t a_off[G::A_INSTR];
     __amdgpu_buffer_rsrc_t ra;   // TILE_A: the tile's A rows
     __amdgpu_buffer_rsrc_t rw;   // the tile's N block of the weights (layout stage 0)
@@ -308,9 +321,21 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   };
   auto make_tile = [&](int uu) __attribute__((always_inline)) -> TileCtx {
     TileCtx t;
-    t.ks = uu / tiles;
-    t.s0 = t.ks * nstages;
-    const int u = uu - t.ks * tiles;
+    int u;
+    if (uu < full) {
+      u = uu;
+      t.ks = 0;
+      t.ns = nst;
+      t.tidx = -1;
+    } else {
+      const int v = uu - full;
+      t.ks = v / tail;
+      const int i = v - t.ks * tail;
+      u = full + i;
+      t.ns = nst / kt;
+      t.tidx = TAILBUF && p.tail_kmax > 1 ? i : -1;
+    }
+    t.s0 = t.ks * t.ns;
     // tile -> (expert, n block, m block).  The tiles of expert e are
     // [mb0 * NB, mb1 * NB) with [mb0, mb1) its BLOCK_M blocks, so u / NB is
     // one of e's blocks, whose tile_info record names e, mb0 and mb1 - mb0.
@@ -562,18 +587,19 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
   //   window, the rest [PA, CPS) in stage s+1's K-step window.  Each copy
   //   has half a stage longer to land, with the same copies per window.
   // The 128- and 256-row MXFP8 tiles, whose weight stream waits on HBM
-  // (the M blocks of an expert share each weight line in L2, so few distinct
-  // lines are in flight), run early; the others measured faster late.  The last stages of a tile issue the first
-  // stages of the workgroup's next tile (when K has enough stages), so the
-  // next tile starts without a pipeline fill and its copies overlap this
-  // tile's epilogue; with no next tile, the copies re-copy the last stage
-  // into a buffer that is not read again (stage indices clamped), which
-  // keeps the copy count per window fixed for the vmcnt bookkeeping.
+  // (the M blocks of an expert share each weight line in L2, so few
+  // distinct lines are in flight), run early; the others measured faster
+  // late.  The last stages of a tile issue the first stages of the
+  // workgroup's next tile (when K has enough stages), so the next tile
+  // starts without a pipeline fill and its copies overlap this tile's
+  // epilogue; with no next tile, the copies re-copy the last stage into a
+  // buffer that is not read again (stage indices clamped), which keeps the
+  // copy count per window fixed for the vmcnt bookkeeping.
   constexpr bool EARLY = FMT == F_MXFP8 && BM >= 128;
   constexpr int LAST = (C::STEPS - 1) * G::CPS / C::STEPS;   // copies in a K-step window
   constexpr int PA = G::CPS - LAST;                          // copies in a boundary window
   static_assert((G::NBUF - 1) * G::CPS < 64, "vmcnt holds 6 bits");
-  const bool chain = nstages >= G::NBUF - 1 + (EARLY ? 1 : 0);
+  constexpr int CHAIN_MIN = G::NBUF - 1 + (EARLY ? 1 : 0);   // stages a tile needs to hand over
   // work unit of round r: in a full round each XCD takes a contiguous run
   // (M blocks sharing a weight block meet in one L2); a partial last round
   // is dealt out across the XCDs in turn, so a small launch uses them all
@@ -611,7 +637,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       tb = make_tile(un);
       tb.par = ta.par ^ 1;
     }
-    const bool chain_next = chain && has_next;
+    // the next tile's first stages are copied during this one's last
+    const bool chain_next = has_next && ta.ns >= CHAIN_MIN && tb.ns >= CHAIN_MIN;
+    const int nstages = ta.ns;
     lds_barrier();        // every wave is done with the previous tile's LDS
     if (has_next) row_dma(tb);
     if (!primed) {
@@ -825,6 +853,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
               __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]), orow + tn * 32);
+          } else if (TAILBUF && ta.tidx >= 0) {
+            // a part of a split-tail tile: [tail tile][part][row][column]
+            const int rloc = wm * TM * 32 + tm * 32 + 8 * (v / 4) + 4 * g + v % 4;
+            float* trow = p.o_tail + ((int64_t)(ta.tidx * kt + ta.ks) * BM + rloc) * GEMM_BN + wn * TN * 32 + l32;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) trow[tn * 32] = acc[tm][tn][v];
           } else {
             float* orow = p.o + ta.ks * p.o_split + col;
 #pragma unroll
@@ -945,6 +979,25 @@ static hipError_t launch_fmt(int layer, int bm, const GemmArgs& a, int grid, hip
     case 64: return launch_fmt_bm<FMT, 64>(layer, a, grid, st);
     case 128: return launch_fmt_bm<FMT, 128>(layer, a, grid, st);
     default: return launch_fmt_bm<FMT, 256>(layer, a, grid, st);
+  }
+}
+
+template <int FMT>
+static int workgroups_fmt(int bm, int grid) {
+  switch (bm) {
+    case 32: return grid * TileGeom<FMT, 32>::OCC;
+    case 64: return grid * TileGeom<FMT, 64>::OCC;
+    case 128: return grid * TileGeom<FMT, 128>::OCC;
+    default: return grid * TileGeom<FMT, 256>::OCC;
+  }
+}
+
+int gemm_workgroups(int fmt, int bm, int grid) {
+  switch (fmt) {
+    case F_BF16: return workgroups_fmt<F_BF16>(bm, grid);
+    case F_MXFP8: return workgroups_fmt<F_MXFP8>(bm, grid);
+    case F_MXFP4: return workgroups_fmt<F_MXFP4>(bm, grid);
+    default: return workgroups_fmt<F_NVFP4>(bm, grid);
   }
 }
 

@@ -57,6 +57,13 @@ struct GemmArgs {
   // L2 of a block-scaled layer with K unsplit: the rows of o are BF16 (RNE of
   // the float32 accumulators), [S, N] uint16
   int o_bf16;
+  // L2 with a split tail (tail_kmax > 1, float32 rows, ksplit 1): the tiles
+  // of the persistent grid's partial last round run as K parts (tail_split);
+  // their parts go to o_tail as [tail tile][part][bm rows][256 columns], the
+  // other tiles' rows to o.  o_tail holds tail_units such units.
+  float* o_tail;
+  int tail_kmax;
+  int tail_units;
   // BLOCK_M.  BF16 layers keep both GEMMs' A operand (the sorted x rows, the
   // L2 input) stage-blocked: [M / bm][K / 32][bm rows][32 values], so a
   // tile's 32-K stage of A is one contiguous run of bm * 64 bytes
@@ -64,6 +71,31 @@ struct GemmArgs {
 };
 
 enum Fmt { F_BF16 = 0, F_MXFP8 = 1, F_MXFP4 = 2, F_NVFP4 = 3 };
+
+// The split tail of an L2 launch over `tiles` whole tiles with nw work slots
+// (the persistent grid's workgroups): when tiles >= nw leaves a partial last
+// round of tail = tiles % nw tiles, those (the last in the grid's order) run
+// as kt K parts each, kt the largest power of two <= kmax with tail * kt <=
+// min(nw, cap) that divides the nst K stages, so the parts fill that round;
+// the first `full` tiles run whole.  kt = 1, tail = 0 when nothing splits.
+// The GEMM and the combine both derive it from the same routing count.
+struct TailSplit {
+  int full, tail, kt;
+};
+__host__ __device__ inline TailSplit tail_split(int tiles, int nw, int kmax, int cap, int nst) {
+  TailSplit r = {tiles, 0, 1};
+  if (kmax < 2 || nw < 1 || tiles < nw || tiles % nw == 0) return r;
+  const int tail = tiles % nw, lim = nw < cap ? nw : cap;
+  for (int kt = kmax; kt >= 2; kt >>= 1) {
+    if (tail * kt <= lim && nst % kt == 0) {
+      r.full = tiles - tail;
+      r.tail = tail;
+      r.kt = kt;
+      return r;
+    }
+  }
+  return r;
+}
 
 // Routing metadata; with block_counts (dispatch_scratch_ints(S, E) int32
 // values) and at least DISPATCH_MANY_MIN_SLOTS slots, the many-workgroup
@@ -94,12 +126,24 @@ void launch_l1_finish(int fmt, const GemmArgs& a, const int32_t* slot_row, const
                       int S, hipStream_t st);
 
 hipError_t launch_gemm(int fmt, int layer, int bm, const GemmArgs& args, int grid, hipStream_t stream);
+// Workgroups of that launch: grid times the tile's workgroups per CU.
+int gemm_workgroups(int fmt, int bm, int grid);
 hipError_t gemm_init(int device);
 
 // Combine (topk_w NULL: every slot weighs 1); gamma non-NULL adds the
 // post-expert RMSNorm.
-void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, const int32_t* slot_row, const float* topk_w,
-                    int T, int k, int kk, int H, const float* gamma, float eps, uint16_t* out, hipStream_t stream);
+// The split tail of the L2 that wrote the rows (o_tail NULL: none): the
+// GemmArgs fields and the L2 launch's work slots, from which the combine
+// derives the same TailSplit as the GEMM.
+struct CombineTail {
+  const float* o_tail;
+  const int32_t* tile_info;
+  const int32_t* meta;
+  int bm, nw, kmax, cap, nst;
+};
+void launch_combine(const float* o, int o_bf16, int nsplit, int64_t o_split, const int32_t* slot_row,
+                    const float* topk_w, int T, int k, int kk, int H, const float* gamma, float eps,
+                    const CombineTail& tail, uint16_t* out, hipStream_t stream);
 // L1 A-operand block scales x_sf [T, sf_ld] -> block-major planes of the
 // sorted rows: out[kb * plane + m] (rows m < offsets[E]); with a_tok, also
 // row_scale[m] = a_tok of the row's token (1 for padding).

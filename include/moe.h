@@ -301,10 +301,13 @@ int moe_forward_profiled(moe_format_t fmt, int num_tokens, int hidden, int inter
  *       l2_activation_scale); BF16 stage-blocked [M / block_m][I / 32]
  *       [block_m][32] BF16 values (a2_sf -1)
  *   o       the L2 output by slot: BF16 [S, H] when l2_rows_bf16, else
- *       float32, l2_ksplit parts of [S, H] one after another
+ *       float32, l2_ksplit parts of [S, H] one after another; a BF16
+ *       layer whose L2 has more tiles than the GPU has work slots splits
+ *       only the tiles of its partial last round, whose rows are then in an
+ *       unlisted parts buffer, not in o
  * The workspace also holds buffers this struct does not list (the
  * GEMMs' per-block tile records, the many-workgroup dispatch's chunk counts,
- * a K-split L1's float32 parts).  The layout is for inspection (tests,
+ * a K-split L1's float32 parts, the split tail's parts).  The layout is for inspection (tests,
  * debugging); it is not a stable interface.  Returns MOE_OK, MOE_E_INVALID
  * (the shape checks of
  * moe_forward) or MOE_E_WORKSPACE.  Host-only. */

@@ -43,6 +43,11 @@ MULTI = {
     for i, fmt in enumerate(["bf16", "mxfp8", "mxfp4", "nvfp4"]) for j, inter in enumerate([1024, SHORT_I[fmt]])
 }
 
+# A BF16 layer whose L2 has more tiles than the grid has workgroups, with a
+# partial last round: ~20 BLOCK_M-256 blocks x 16 column blocks = ~320 tiles,
+# so the last ~64 run split in 4 K parts (the split tail) and the others whole.
+TAIL = MoEConfig("bf16_tail", 60, "bf16", 2048, 4096, 512, 8, 2, routing="softmax_uniform")
+
 _CACHE = {}
 
 
@@ -107,11 +112,34 @@ def test_forward_several_tiles_per_workgroup(name, bm):
     compare(MULTI[name], block_m=bm)
 
 
+@pytest.mark.parametrize("bm", [0, 128])
+def test_forward_bf16_split_tail(bm):
+    """The L2's partial last round split in K parts, the other tiles whole;
+    the combine takes each slot's columns from the tile that computed them."""
+    compare(TAIL, block_m=bm)
+
+
+def test_forward_bf16_split_tail_with_norm():
+    """The post-expert RMSNorm combine over a split-tail L2."""
+    cfg = TAIL
+    x, ids, wts, w = inputs(cfg)
+    gamma = np.random.default_rng(9).uniform(0.5, 1.5, cfg.H)
+    norm = (gamma, 1e-6)
+    y, _ = run_layer(cfg.fmt, x, ids, wts, w, norm=norm)
+    pre = moe_reference(cfg.fmt, x, ids, wts, w)
+    ref = moe_reference(cfg.fmt, x, ids, wts, w, norm=norm)
+    rel, excess, alt = check_layer(cfg.fmt, y, ref, x, ids, wts, w, norm=norm, y_pre=pre)
+    print(f"bf16_tail + norm: max|err|/RMS = {rel:.3e}")
+    assert excess <= 0, (rel, excess)
+
+
 @pytest.mark.parametrize("name", sorted(MULTI))
 def test_forward_independent_of_block_m(name):
     """Every output element's K sums run in the same order whatever the tile
     height, so all BLOCK_M give bit-identical layers (a check of the tiling
-    and the copy pipeline that needs no tolerance)."""
+    and the copy pipeline that needs no tolerance).  These layers have fewer
+    L2 tiles than the grid has workgroups, so no split tail (whose split
+    tiles depend on the tile height) applies."""
     cfg = MULTI[name]
     x, ids, wts, w = inputs(cfg)
     w2in, _ = l2_scale(cfg)
