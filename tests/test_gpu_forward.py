@@ -43,10 +43,14 @@ MULTI = {
     for i, fmt in enumerate(["bf16", "mxfp8", "mxfp4", "nvfp4"]) for j, inter in enumerate([1024, SHORT_I[fmt]])
 }
 
-# A BF16 layer whose L2 has more tiles than the grid has workgroups, with a
-# partial last round: ~20 BLOCK_M-256 blocks x 16 column blocks = ~320 tiles,
-# so the last ~64 run split in 4 K parts (the split tail) and the others whole.
+# BF16 layers whose L2 has more tiles than the grid has workgroups, with a
+# partial last round that runs split in K parts (the split tail) while the
+# other tiles run whole: 22 BLOCK_M-256 blocks x 16 column blocks = 352
+# tiles, the last 96 in 2 parts of 8 stages; and x 24 column blocks = 528
+# tiles, the last 16 in 4 parts of 2 stages each (too short to hand stages
+# over to the next tile, so each part fills the copy ring itself).
 TAIL = MoEConfig("bf16_tail", 60, "bf16", 2048, 4096, 512, 8, 2, routing="softmax_uniform")
+TAIL_SHORT = MoEConfig("bf16_tail_short", 60, "bf16", 2048, 6144, 256, 8, 2, routing="softmax_uniform")
 
 _CACHE = {}
 
@@ -112,11 +116,11 @@ def test_forward_several_tiles_per_workgroup(name, bm):
     compare(MULTI[name], block_m=bm)
 
 
-@pytest.mark.parametrize("bm", [0, 128])
-def test_forward_bf16_split_tail(bm):
+@pytest.mark.parametrize("cfg,bm", [(TAIL, 0), (TAIL, 128), (TAIL_SHORT, 0)], ids=["bm0", "bm128", "short_parts"])
+def test_forward_bf16_split_tail(cfg, bm):
     """The L2's partial last round split in K parts, the other tiles whole;
     the combine takes each slot's columns from the tile that computed them."""
-    compare(TAIL, block_m=bm)
+    compare(cfg, block_m=bm)
 
 
 def test_forward_bf16_split_tail_with_norm():
