@@ -834,6 +834,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       const bool o16 = FMT != F_BF16 && LAYER == 2 && p.o_bf16;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
+        // split tail: this row block's rows in the tile's part
+        float* const tail_base =
+            TAILBUF && ta.tidx >= 0
+                ? p.o_tail + ((int64_t)(ta.tidx * kt + ta.ks) * BM + wm * TM * 32 + tm * 32) * GEMM_BN +
+                      wn * TN * 32 + l32
+                : nullptr;
         int slots[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -853,14 +859,11 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
               __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]), orow + tn * 32);
-          } else if (TAILBUF && ta.tidx >= 0) {
-            // a part of a split-tail tile: [tail tile][part][row][column]
-            const int rloc = wm * TM * 32 + tm * 32 + 8 * (v / 4) + 4 * g + v % 4;
-            float* trow = p.o_tail + ((int64_t)(ta.tidx * kt + ta.ks) * BM + rloc) * GEMM_BN + wn * TN * 32 + l32;
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) trow[tn * 32] = acc[tm][tn][v];
           } else {
+            // by slot; a part of a split-tail tile: [tail tile][part][row][column]
             float* orow = p.o + ta.ks * p.o_split + col;
+            if (TAILBUF && ta.tidx >= 0)
+              orow = tail_base + (8 * (v / 4) + 4 * g + v % 4) * GEMM_BN;
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
           }
