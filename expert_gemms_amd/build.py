@@ -50,12 +50,31 @@ def asan_runtime():
     return hits[-1] if hits else None
 
 
+# the GEMM kernels' register report (VGPRs, spills, scratch per kernel), written
+# by the library build for tests/test_gemm_registers.py
+GEMM_USAGE = os.path.join(BUILD_DIR, "gemm.resource-usage.txt")
+GEMM_USAGE_SOURCES = ("gemm.hip", "common.h", "launch.h", "l2input.h")
+
+
+def gemm_sources_sha256():
+    h = hashlib.sha256(" ".join([HIPCC, *FLAGS]).encode())
+    for f in GEMM_USAGE_SOURCES:
+        with open(os.path.join(SRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()
+
+
 def _compile(src, build_dir=BUILD_DIR, extra=()):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    usage = not extra and os.path.basename(src) == "gemm.hip"
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj] + (["-Rpass-analysis=kernel-resource-usage"] if usage else [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if usage:
+        with open(GEMM_USAGE, "w") as fh:
+            fh.write(f"sources sha256 {gemm_sources_sha256()}\n")
+            fh.write("\n".join(l for l in r.stderr.splitlines() if "remark" in l) + "\n")
     return obj
 
 
