@@ -16,6 +16,8 @@
 // per-wave counts (per expert) and the BLOCK_M-padded totals (over experts).
 // Pass 3 walks the batches again in order and scatters every slot to
 // offset + (earlier slots of its expert), which is the stable order.
+#include <type_traits>
+
 #include "common.h"
 #include "l2input.h"
 #include "launch.h"
@@ -44,15 +46,35 @@ __device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
   return e >= 0 ? m : 0ull;
 }
 
+// Experts of lane l's slots in DGROUP consecutive 64-slot batches from b
+// (-1: past s1 or dropped).  All DGROUP loads are issued before any is used, so a pass
+// over a wave's slots waits out one load latency per DGROUP batches, not one
+// per batch.
+constexpr int DGROUP = 8;
+
+__device__ __forceinline__ void group_experts(const int32_t* __restrict__ topk_ids, int b, int s1, int kk, int k,
+                                              int start, int n_loc, int l, int (&e)[DGROUP]) {
+#pragma unroll
+  for (int i = 0; i < DGROUP; ++i) {
+    const int s = b + i * WAVE + l;
+    e[i] = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+  }
+}
+
 // Counting pass over one wave's slots [s0, s1): hist_w[e] += its slots of
 // expert e (the lowest lane of each group of equal experts adds the group).
 __device__ __forceinline__ void wave_count(const int32_t* __restrict__ topk_ids, int s0, int s1, int kk, int k,
                                            int start, int n_loc, int nbits, int* hist_w, int l) {
-  for (int b = s0; b < s1; b += WAVE) {
-    int s = b + l;
-    int e = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
-    uint64_t m = match_mask(e, nbits);
-    if (e >= 0 && (__builtin_ctzll(m) == l)) hist_w[e] += __builtin_popcountll(m);
+  for (int b = s0; b < s1; b += DGROUP * WAVE) {
+    int eg[DGROUP];
+    group_experts(topk_ids, b, s1, kk, k, start, n_loc, l, eg);
+#pragma unroll
+    for (int i = 0; i < DGROUP; ++i) {
+      if (b + i * WAVE >= s1) break;
+      const int e = eg[i];
+      uint64_t m = match_mask(e, nbits);
+      if (e >= 0 && (__builtin_ctzll(m) == l)) hist_w[e] += __builtin_popcountll(m);
+    }
   }
 }
 
@@ -63,22 +85,29 @@ __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ topk_id
                                              int start, int n_loc, int nbits, int* hist_w, int l,
                                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row) {
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  for (int b = s0; b < s1; b += WAVE) {
-    int s = b + l;
-    bool live = s < s1;
-    int e = live ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
-    uint64_t m = match_mask(e, nbits);
-    if (e >= 0) {
-      int pos = hist_w[e] + __builtin_popcountll(m & lt_mask);
-      sorted_slot[pos] = s;
-      slot_row[s] = pos;
-    } else if (live) {
-      slot_row[s] = -1;
+  for (int b0 = s0; b0 < s1; b0 += DGROUP * WAVE) {
+    int eg[DGROUP];
+    group_experts(topk_ids, b0, s1, kk, k, start, n_loc, l, eg);
+#pragma unroll
+    for (int i = 0; i < DGROUP; ++i) {
+      const int b = b0 + i * WAVE;
+      if (b >= s1) break;
+      const int s = b + l;
+      const bool live = s < s1;
+      const int e = eg[i];
+      uint64_t m = match_mask(e, nbits);
+      if (e >= 0) {
+        int pos = hist_w[e] + __builtin_popcountll(m & lt_mask);
+        sorted_slot[pos] = s;
+        slot_row[s] = pos;
+      } else if (live) {
+        slot_row[s] = -1;
+      }
+      // every lane has read its base before the group leader bumps it
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0 && __builtin_ctzll(m) == l) hist_w[e] += __builtin_popcountll(m);
+      __builtin_amdgcn_wave_barrier();
     }
-    // every lane has read its base before the group leader bumps it
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0 && __builtin_ctzll(m) == l) hist_w[e] += __builtin_popcountll(m);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -367,19 +396,34 @@ k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, 
   __shared__ int wave_tot[DISPATCH_WAVES];
   __shared__ int s_off[MAX_LOCAL_EXPERTS + 1];
   const int tid = threadIdx.x, w = tid / WAVE, l = tid % WAVE;
-  // the chunks' counts of expert tid, 16 loads in flight at a time (a
-  // load-add-store chain per chunk would wait out each load's latency)
-  constexpr int BATCH = 16;
+  // the chunks' counts of expert tid: up to RCHUNKS chunks all loaded at
+  // once and kept in registers (one load latency, then one round of
+  // stores); more chunks 16 loads at a time, with a second pass adding the
+  // offset (a load-add-store chain per chunk would wait out each load)
+  constexpr int RCHUNKS = 64, BATCH = 16;
+  const bool in_regs = nchunks <= RCHUNKS;
+  int n[RCHUNKS];
   int run = 0;
   if (tid < E) {
-    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-      int n[BATCH];
+    if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) n[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+      for (int i = 0; i < RCHUNKS; ++i) n[i] = i < nchunks ? block_counts[(int64_t)i * E + tid] : 0;
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = run;
-        run += n[i];
+      for (int i = 0; i < RCHUNKS; ++i) {
+        const int c = n[i];
+        n[i] = run;
+        run += c;
+      }
+    } else {
+      for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+        int nb[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) nb[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = run;
+          run += nb[i];
+        }
       }
     }
     counts[tid] = run;
@@ -400,13 +444,19 @@ k_dispatch_scan(int nchunks, int E, int bm, int32_t* __restrict__ block_counts, 
   for (int ww = 0; ww < DISPATCH_WAVES; ++ww) total += wave_tot[ww];
   if (tid < E) {
     offsets[tid] = off;
-    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
-      int b[BATCH];
+    if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) b[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+      for (int i = 0; i < RCHUNKS; ++i)
+        if (i < nchunks) block_counts[(int64_t)i * E + tid] = n[i] + off;
+    } else {
+      for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+        int b[BATCH];
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i)
-        if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = b[i] + off;
+        for (int i = 0; i < BATCH; ++i) b[i] = c0 + i < nchunks ? block_counts[(int64_t)(c0 + i) * E + tid] : 0;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          if (c0 + i < nchunks) block_counts[(int64_t)(c0 + i) * E + tid] = b[i] + off;
+      }
     }
     for (int r = off + run; r < off + v; ++r) sorted_slot[r] = -1;
     s_off[tid] = off;
@@ -502,15 +552,19 @@ bool launch_dispatch_quant_mx(const int32_t* topk_ids, int T, int k, int n_sh, i
 // a tile's scales for one K block are BLOCK_M consecutive bytes.  Row m of
 // the sorted order takes the scale row of token sorted_slot[m] / kk; a
 // padding row, and the rows from offsets[E] to the next multiple of 4, take
-// `fill`.  A thread takes 4 rows and 8 planes (blockIdx.y: the plane
-// group) and stores a dword of 4 rows per plane (256 consecutive bytes per
-// wave).  With a_tok (NVFP4), the first plane group also writes each row's
-// token scale to row_scale (1 for a padding row).
+// `fill`.  A thread takes 4 rows and P planes (blockIdx.y: the plane group;
+// P = 16 where the rows' scale bytes split into 16-byte pieces, else 8) and
+// stores a dword of 4 rows per plane (256 consecutive bytes per wave).
+// With a_tok (NVFP4), the first plane group also writes each row's token
+// scale to row_scale (1 for a padding row).
+template <int P>
 __global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ sorted_slot,
                                                    const int32_t* __restrict__ offsets, int E, int kk,
                                                    const uint8_t* __restrict__ x_sf, int sf_ld, int64_t plane,
                                                    uint8_t fill, uint8_t* __restrict__ out,
                                                    const float* __restrict__ a_tok, float* __restrict__ row_scale) {
+  static_assert(P == 8 || P == 16, "8 or 16 planes per thread");
+  using V = typename std::conditional<P == 16, uint4, uint2>::type;
   const int m = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int M = offsets[E];
   if (m >= M) return;
@@ -523,21 +577,27 @@ __global__ void __launch_bounds__(256) k_gather_sf(const int32_t* __restrict__ s
     src[i] = x_sf + (int64_t)(real[i] ? sl / kk : 0) * sf_ld;
     if (a_tok && blockIdx.y == 0 && m + i < M) row_scale[m + i] = real[i] ? a_tok[sl / kk] : 1.0f;
   }
-  {
-    const int kb = blockIdx.y * 8;
-    uint2 v[4];
+  const int kb = blockIdx.y * P;
+  uint32_t v[4][P / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *(const uint2*)(src[i] + kb);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t b = real[i] ? ((j < 4 ? v[i].x : v[i].y) >> (8 * (j & 3))) & 0xFF : fill;
-        word |= b << (8 * i);
-      }
-      *(uint32_t*)(out + (int64_t)(kb + j) * plane + m) = word;
+  for (int i = 0; i < 4; ++i) {
+    const V x = *(const V*)(src[i] + kb);
+    v[i][0] = x.x;
+    v[i][1] = x.y;
+    if constexpr (P == 16) {
+      v[i][2] = x.z;
+      v[i][3] = x.w;
     }
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b = real[i] ? (v[i][j / 4] >> (8 * (j & 3))) & 0xFF : fill;
+      word |= b << (8 * i);
+    }
+    *(uint32_t*)(out + (int64_t)(kb + j) * plane + m) = word;
   }
 }
 
@@ -546,8 +606,12 @@ void launch_gather_sf(const int32_t* sorted_slot, const int32_t* offsets, int E,
                       float* row_scale, hipStream_t stream) {
   const unsigned blocks = (unsigned)((max_rows + 1023) / 1024);
   if (blocks == 0 || sf_ld < 8) return;
-  hipLaunchKernelGGL(k_gather_sf, dim3(blocks, (unsigned)(sf_ld / 8)), dim3(256), 0, stream, sorted_slot, offsets, E, kk, x_sf, sf_ld,
-                     plane, fill, out, a_tok, row_scale);
+  if (sf_ld % 16 == 0)
+    hipLaunchKernelGGL(k_gather_sf<16>, dim3(blocks, (unsigned)(sf_ld / 16)), dim3(256), 0, stream, sorted_slot,
+                       offsets, E, kk, x_sf, sf_ld, plane, fill, out, a_tok, row_scale);
+  else
+    hipLaunchKernelGGL(k_gather_sf<8>, dim3(blocks, (unsigned)(sf_ld / 8)), dim3(256), 0, stream, sorted_slot,
+                       offsets, E, kk, x_sf, sf_ld, plane, fill, out, a_tok, row_scale);
 }
 
 // BF16 layers: the L1 GEMM's A rows in sorted order and stage-blocked
