@@ -95,6 +95,69 @@ __global__ void __launch_bounds__(256) k_quant_nv(const void* __restrict__ src, 
   }
 }
 
+// NVFP4 dispatch quantisation of BF16 rows, each with its own global scale
+// from its amax: the arithmetic of k_quant_nv, one wave per row (four rows
+// per workgroup, no workgroup barrier) and lane l holding 32 consecutive
+// values, two 16-element blocks, of each 2048-column chunk.  The row is read
+// twice, for its amax and for its codes; the second read finds it in cache.
+__global__ void __launch_bounds__(256) k_quant_nv_rows(const uint16_t* __restrict__ src, int64_t rows, int cols,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                       float* __restrict__ row_g) {
+#pragma clang fp contract(off)
+  const int l = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* p = src + row * cols;
+  auto load32 = [&](int c, float (&v)[32]) __attribute__((always_inline)) {
+    const uint4* q = (const uint4*)(p + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = q[i];
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = u2f(wd[j] << 16);
+        v[8 * i + 2 * j + 1] = u2f(wd[j] & 0xFFFF0000u);
+      }
+    }
+  };
+  float amax = 0.0f;
+  for (int c = l * 32; c < cols; c += 64 * 32) {
+    float v[32];
+    load32(c, v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  }
+  amax = group_max<6>(amax);
+  const float g = amax > 0.0f ? amax / 2688.0f : 1.0f;
+  if (l == 0) row_g[row] = g;
+  const float six_g = 6.0f * g;
+  for (int c = l * 32; c < cols; c += 64 * 32) {
+    float v[32];
+    load32(c, v);
+    uint32_t w[4] = {0, 0, 0, 0}, bs2 = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* b = v + 16 * h;
+      float bmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bmax = __builtin_fmaxf(bmax, __builtin_fabsf(b[i]));
+      const uint32_t bs = e4m3_encode(bmax / six_g);
+      const float bsv = e4m3_decode(bs);
+      if (bsv != 0.0f) {
+        const float r = 1.0f / (bsv * g);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          w[2 * h + q] = e2m1_x4(b[8 * q] * r, b[8 * q + 1] * r, b[8 * q + 2] * r, b[8 * q + 3] * r) |
+                         (e2m1_x4(b[8 * q + 4] * r, b[8 * q + 5] * r, b[8 * q + 6] * r, b[8 * q + 7] * r) << 16);
+      }
+      bs2 |= bs << (8 * h);
+    }
+    *(uint16_t*)(scales + row * (cols / 16) + c / 16) = (uint16_t)bs2;
+    *(uint4*)(codes + (row * cols + c) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Per-expert amax -> NVFP4 global scale amax / (6 * 448) (1 if zero).
 __global__ void __launch_bounds__(256) k_weight_gscale(const float* __restrict__ src, int64_t per_expert,
                                                        float* __restrict__ gscale) {
@@ -133,6 +196,9 @@ void launch_quant_nv(bool f32, int64_t rows, int cols, const void* src, uint8_t*
   if (f32)
     hipLaunchKernelGGL((k_quant_nv<true>), dim3((unsigned)rows), dim3(256), 0, st, src, cols, codes, scales, row_g,
                        fixed_g, rows_per_g);
+  else if (!fixed_g)
+    hipLaunchKernelGGL(k_quant_nv_rows, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const uint16_t*)src, rows,
+                       cols, codes, scales, row_g);
   else
     hipLaunchKernelGGL((k_quant_nv<false>), dim3((unsigned)rows), dim3(256), 0, st, src, cols, codes, scales, row_g,
                        fixed_g, rows_per_g);

@@ -39,7 +39,7 @@ def test_quantize_x_mxfp8_bit_exact(T, H):
     assert np.array_equal(codes.cpu().numpy(), q)
 
 
-@pytest.mark.parametrize("T,H", [(7, 256), (130, 2048)])
+@pytest.mark.parametrize("T,H", [(7, 256), (130, 2048), (9, 2304), (7, 6144)])
 def test_quantize_x_nvfp4_bit_exact(T, H):
     xb = special_x(T, H, 3 * T + H)
     codes = torch.empty((T, H // 2), dtype=torch.uint8, device="cuda")
