@@ -808,15 +808,22 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         for (int pp = 0; pp < TN / 2; ++pp) {
           const int icol0 = nb * (GEMM_BN / 2) + (wn * (TN / 2) + pp) * 32;
           float a[16];
+          // the clamp's presence is chosen once per 16 activations
+          auto act16 = [&](auto clampc) __attribute__((always_inline)) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float gv = acc[tm][2 * pp][v], uv = acc[tm][2 * pp + 1][v];
-            if constexpr (C::NV) {
-              gv *= alpha;
-              uv *= alpha;
+            for (int v = 0; v < 16; ++v) {
+              float gv = acc[tm][2 * pp][v], uv = acc[tm][2 * pp + 1][v];
+              if constexpr (C::NV) {
+                gv *= alpha;
+                uv *= alpha;
+              }
+              a[v] = act_swiglu_c<decltype(clampc)::value>(gv, uv, p);
             }
-            a[v] = act_swiglu(gv, uv, p);
-          }
+          };
+          if (p.has_clamp)
+            act16(std::true_type{});
+          else
+            act16(std::false_type{});
           store_l2_input_rows<FMT>(a, row, icol0, g, p);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -830,44 +837,59 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // block-scaled L2 with K unsplit: BF16 rows (the output dtype the
       // combine reads), stored non-temporally (written once, read once by
       // the combine, so they need not displace the weights from the
-      // caches); else float32 rows (BF16 layers, K parts, split L1)
-      const bool o16 = FMT != F_BF16 && LAYER == 2 && p.o_bf16;
+      // caches); else float32 rows (BF16 layers, K parts, split L1).  MODE
+      // 0: float32, 1: BF16, 2: chosen per row (the MX formats choose once
+      // per tile, which measured faster for them and slower for the others)
+      auto l2_epilogue = [&](auto modec) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(modec)::value;
+        const bool o16 = MODE == 2 ? FMT != F_BF16 && LAYER == 2 && p.o_bf16 : MODE == 1;
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        // split tail: this row block's rows in the tile's part
-        float* const tail_base =
-            TAILBUF && ta.tidx >= 0
-                ? p.o_tail + ((int64_t)(ta.tidx * kt + ta.ks) * BM + wm * TM * 32 + tm * 32) * GEMM_BN +
-                      wn * TN * 32 + l32
-                : nullptr;
-        int slots[16];
+        for (int tm = 0; tm < TM; ++tm) {
+          // split tail: this row block's rows in the tile's part
+          float* const tail_base =
+              TAILBUF && ta.tidx >= 0
+                  ? p.o_tail + ((int64_t)(ta.tidx * kt + ta.ks) * BM + wm * TM * 32 + tm * 32) * GEMM_BN +
+                        wn * TN * 32 + l32
+                  : nullptr;
+          int slots[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 s4 = *(const int4*)(rslot + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
-          slots[4 * q] = s4.x;
-          slots[4 * q + 1] = s4.y;
-          slots[4 * q + 2] = s4.z;
-          slots[4 * q + 3] = s4.w;
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int4 s4 = *(const int4*)(rslot + wm * TM * 32 + tm * 32 + 8 * q + 4 * g);
+            slots[4 * q] = s4.x;
+            slots[4 * q + 1] = s4.y;
+            slots[4 * q + 2] = s4.z;
+            slots[4 * q + 3] = s4.w;
+          }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int slot = slots[v];
-          if (slot < 0) continue;
-          const int64_t col = (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
-          if (o16) {
-            uint16_t* orow = (uint16_t*)p.o + col;
+          for (int v = 0; v < 16; ++v) {
+            const int slot = slots[v];
+            if (slot < 0) continue;
+            const int64_t col = (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
+            if (o16) {
+              uint16_t* orow = (uint16_t*)p.o + col;
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-              __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]), orow + tn * 32);
-          } else {
-            // by slot; a part of a split-tail tile: [tail tile][part][row][column]
-            float* orow = p.o + ta.ks * p.o_split + col;
-            if (TAILBUF && ta.tidx >= 0)
-              orow = tail_base + (8 * (v / 4) + 4 * g + v % 4) * GEMM_BN;
+              for (int tn = 0; tn < TN; ++tn)
+                __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]),
+                                            orow + tn * 32);
+            } else {
+              // by slot; a part of a split-tail tile: [tail tile][part][row][column]
+              float* orow = p.o + ta.ks * p.o_split + col;
+              if (TAILBUF && ta.tidx >= 0)
+                orow = tail_base + (8 * (v / 4) + 4 * g + v % 4) * GEMM_BN;
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
+              for (int tn = 0; tn < TN; ++tn)
+                orow[tn * 32] = C::NV && LAYER == 2 ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v];
+            }
           }
         }
+      };
+      if constexpr ((FMT == F_MXFP8 || FMT == F_MXFP4) && LAYER == 2) {
+        if (p.o_bf16)
+          l2_epilogue(IC<1>{});
+        else
+          l2_epilogue(IC<0>{});
+      } else {
+        l2_epilogue(IC<2>{});
       }
     }
     if (has_next) ta = tb;

@@ -41,13 +41,20 @@ __device__ __forceinline__ uint32_t e4m3_x1_mx(float a) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xFFu;
 }
 
-__device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
-  if (p.has_clamp) {
+// CLAMP: whether the clamp applies (p.has_clamp), fixed at compile time by
+// callers that evaluate many activations per branch.
+template <bool CLAMP>
+__device__ __forceinline__ float act_swiglu_c(float g, float u, const GemmArgs& p) {
+  if constexpr (CLAMP) {
     g = __builtin_fminf(g, p.clamp);
     u = __builtin_fminf(__builtin_fmaxf(u, -p.clamp), p.clamp);
   }
   float s = __builtin_amdgcn_rcpf(1.0f + __expf(-p.alpha * g));
   return g * s * (u + p.beta);
+}
+
+__device__ __forceinline__ float act_swiglu(float g, float u, const GemmArgs& p) {
+  return p.has_clamp ? act_swiglu_c<true>(g, u, p) : act_swiglu_c<false>(g, u, p);
 }
 
 // Activation value a of sorted row `row`, intermediate column icol.  The 32
