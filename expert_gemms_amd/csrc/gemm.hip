@@ -839,10 +839,12 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // the combine, so they need not displace the weights from the
       // caches); else float32 rows (BF16 layers, K parts, split L1).  MODE
       // 0: float32, 1: BF16, 2: chosen per row (the MX formats choose once
-      // per tile, which measured faster for them and slower for the others)
+      // per tile, which measured faster for them and slower for the others),
+      // 3: BF16 with fewer than 2^32 elements in o, so a row's offset is a
+      // 24-bit product (slot < 2^24 as N >= 256), not a 64-bit one
       auto l2_epilogue = [&](auto modec) __attribute__((always_inline)) {
         constexpr int MODE = decltype(modec)::value;
-        const bool o16 = MODE == 2 ? FMT != F_BF16 && LAYER == 2 && p.o_bf16 : MODE == 1;
+        const bool o16 = MODE == 2 ? FMT != F_BF16 && LAYER == 2 && p.o_bf16 : MODE == 1 || MODE == 3;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
           // split tail: this row block's rows in the tile's part
@@ -866,7 +868,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
             if (slot < 0) continue;
             const int64_t col = (int64_t)slot * p.N + nb * GEMM_BN + wn * TN * 32 + l32;
             if (o16) {
-              uint16_t* orow = (uint16_t*)p.o + col;
+              uint16_t* orow =
+                  MODE == 3 ? (uint16_t*)p.o + (__umul24((uint32_t)slot, (uint32_t)p.N) +
+                                                (uint32_t)(nb * GEMM_BN + wn * TN * 32 + l32))
+                            : (uint16_t*)p.o + col;
 #pragma unroll
               for (int tn = 0; tn < TN; ++tn)
                 __builtin_nontemporal_store(bf16_rne(C::NV ? acc[tm][tn][v] * alpha2 : acc[tm][tn][v]),
@@ -884,7 +889,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
         }
       };
       if constexpr ((FMT == F_MXFP8 || FMT == F_MXFP4) && LAYER == 2) {
-        if (p.o_bf16)
+        if (p.o_bf16 && p.o_split < (int64_t{1} << 32))
+          l2_epilogue(IC<3>{});
+        else if (p.o_bf16)
           l2_epilogue(IC<1>{});
         else
           l2_epilogue(IC<0>{});
