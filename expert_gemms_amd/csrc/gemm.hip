@@ -838,10 +838,9 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // combine reads), stored non-temporally (written once, read once by
       // the combine, so they need not displace the weights from the
       // caches); else float32 rows (BF16 layers, K parts, split L1).  MODE
-      // 0: float32, 1: BF16, 2: chosen per row (the MX formats choose once
-      // per tile, which measured faster for them and slower for the others),
-      // 3: BF16 with fewer than 2^32 elements in o, so a row's offset is a
-      // 24-bit product (slot < 2^24 as N >= 256), not a 64-bit one
+      // 0: float32, 1: BF16, 2: chosen per row (BF16 layers), 3: BF16 with
+      // fewer than 2^32 elements in o, so a row's offset is a 24-bit product
+      // (slot < 2^24 as N >= 256), not a 64-bit one
       auto l2_epilogue = [&](auto modec) __attribute__((always_inline)) {
         constexpr int MODE = decltype(modec)::value;
         const bool o16 = MODE == 2 ? FMT != F_BF16 && LAYER == 2 && p.o_bf16 : MODE == 1 || MODE == 3;
@@ -888,7 +887,8 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           }
         }
       };
-      if constexpr ((FMT == F_MXFP8 || FMT == F_MXFP4) && LAYER == 2) {
+      // (not the NVFP4 256-row L2, whose registers the second copy overruns)
+      if constexpr (FMT != F_BF16 && LAYER == 2 && !(C::NV && BM == 256)) {
         if (p.o_bf16 && p.o_split < (int64_t{1} << 32))
           l2_epilogue(IC<3>{});
         else if (p.o_bf16)
