@@ -46,30 +46,35 @@ __device__ __forceinline__ uint64_t match_mask(int e, int nbits) {
   return e >= 0 ? m : 0ull;
 }
 
-// Experts of lane l's slots in DGROUP consecutive 64-slot batches from b
-// (-1: past s1 or dropped).  All DGROUP loads are issued before any is used, so a pass
-// over a wave's slots waits out one load latency per DGROUP batches, not one
-// per batch.
-constexpr int DGROUP = 8;
-
+// Experts of lane l's slots in G consecutive 64-slot batches from b (-1:
+// past s1 or dropped).  All G loads are issued before any is used, so a pass
+// over a wave's slots waits out one load latency per G batches, not one per
+// batch.  The many-workgroup passes take 8 batches at a time; the
+// single-workgroup dispatch one (at decode sizes, where a wave has one batch
+// or none, the wider form measured slower).
+template <int G>
 __device__ __forceinline__ void group_experts(const int32_t* __restrict__ topk_ids, int b, int s1, int kk, int k,
-                                              int start, int n_loc, int l, int (&e)[DGROUP]) {
+                                              int start, int n_loc, int l, int (&e)[G]) {
 #pragma unroll
-  for (int i = 0; i < DGROUP; ++i) {
-    const int s = b + i * WAVE + l;
-    e[i] = s < s1 ? slot_expert(topk_ids, s, kk, k, start, n_loc) : -1;
+  for (int i = 0; i < G; ++i) {
+    e[i] = -1;
+    if (b + i * WAVE < s1) {   // uniform: no work for batches past the end
+      const int s = b + i * WAVE + l;
+      if (s < s1) e[i] = slot_expert(topk_ids, s, kk, k, start, n_loc);
+    }
   }
 }
 
 // Counting pass over one wave's slots [s0, s1): hist_w[e] += its slots of
 // expert e (the lowest lane of each group of equal experts adds the group).
+template <int G>
 __device__ __forceinline__ void wave_count(const int32_t* __restrict__ topk_ids, int s0, int s1, int kk, int k,
                                            int start, int n_loc, int nbits, int* hist_w, int l) {
-  for (int b = s0; b < s1; b += DGROUP * WAVE) {
-    int eg[DGROUP];
-    group_experts(topk_ids, b, s1, kk, k, start, n_loc, l, eg);
+  for (int b = s0; b < s1; b += G * WAVE) {
+    int eg[G];
+    group_experts<G>(topk_ids, b, s1, kk, k, start, n_loc, l, eg);
 #pragma unroll
-    for (int i = 0; i < DGROUP; ++i) {
+    for (int i = 0; i < G; ++i) {
       if (b + i * WAVE >= s1) break;
       const int e = eg[i];
       uint64_t m = match_mask(e, nbits);
@@ -81,15 +86,16 @@ __device__ __forceinline__ void wave_count(const int32_t* __restrict__ topk_ids,
 // Scatter pass over one wave's slots [s0, s1) in order: slot s of expert e
 // goes to row hist_w[e] + (earlier slots of e in its batch), then the group
 // leader advances hist_w[e]; a dropped slot gets slot_row -1.
+template <int G>
 __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ topk_ids, int s0, int s1, int kk, int k,
                                              int start, int n_loc, int nbits, int* hist_w, int l,
                                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row) {
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  for (int b0 = s0; b0 < s1; b0 += DGROUP * WAVE) {
-    int eg[DGROUP];
-    group_experts(topk_ids, b0, s1, kk, k, start, n_loc, l, eg);
+  for (int b0 = s0; b0 < s1; b0 += G * WAVE) {
+    int eg[G];
+    group_experts<G>(topk_ids, b0, s1, kk, k, start, n_loc, l, eg);
 #pragma unroll
-    for (int i = 0; i < DGROUP; ++i) {
+    for (int i = 0; i < G; ++i) {
       const int b = b0 + i * WAVE;
       if (b >= s1) break;
       const int s = b + l;
@@ -150,7 +156,7 @@ __device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids
   const int s0 = min(w * per, S), s1 = min(s0 + per, S);
 
   // pass 1: per-wave histogram
-  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
+  wave_count<1>(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
   __syncthreads();
 
   // pass 2a: expert tid: exclusive scan of its per-wave counts; padded size
@@ -191,7 +197,7 @@ __device__ __forceinline__ void dispatch_wg(const int32_t* __restrict__ topk_ids
   __syncthreads();
 
   // pass 3: stable scatter
-  wave_scatter(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
+  wave_scatter<1>(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
 
   // padding rows and the tile -> expert tables
   if (tid < E)
@@ -379,7 +385,7 @@ k_dispatch_count(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh, i
   for (int i = tid; i < DC_WAVES * MAX_LOCAL_EXPERTS; i += DC_WAVES * WAVE) (&hist[0][0])[i] = 0;
   __syncthreads();
   const int s0 = min(blockIdx.x * DCHUNK + w * DC_PER_WAVE, S), s1 = min(s0 + DC_PER_WAVE, S);
-  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
+  wave_count<8>(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
   __syncthreads();
   for (int e = tid; e < E; e += DC_WAVES * WAVE) {
     int c = 0;
@@ -483,7 +489,7 @@ k_dispatch_scatter(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh,
   for (int i = tid; i < DC_WAVES * MAX_LOCAL_EXPERTS; i += DC_WAVES * WAVE) (&hist[0][0])[i] = 0;
   __syncthreads();
   const int s0 = min(blockIdx.x * DCHUNK + w * DC_PER_WAVE, S), s1 = min(s0 + DC_PER_WAVE, S);
-  wave_count(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
+  wave_count<8>(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l);
   __syncthreads();
   // each wave's first row per expert: the chunk's base plus the earlier waves
   for (int e = tid; e < E; e += DC_WAVES * WAVE) {
@@ -496,7 +502,7 @@ k_dispatch_scatter(const int32_t* __restrict__ topk_ids, int T, int k, int n_sh,
     }
   }
   __syncthreads();
-  wave_scatter(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
+  wave_scatter<8>(topk_ids, s0, s1, kk, k, start, n_loc, nbits, hist[w], l, sorted_slot, slot_row);
 }
 
 int64_t dispatch_scratch_ints(int64_t S, int E) { return (S + DCHUNK - 1) / DCHUNK * E; }
