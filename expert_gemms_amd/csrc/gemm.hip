@@ -838,9 +838,10 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
       // combine reads), stored non-temporally (written once, read once by
       // the combine, so they need not displace the weights from the
       // caches); else float32 rows (BF16 layers, K parts, split L1).  MODE
-      // 0: float32, 1: BF16, 2: chosen per row (BF16 layers), 3: BF16 with
-      // fewer than 2^32 elements in o, so a row's offset is a 24-bit product
-      // (slot < 2^24 as N >= 256), not a 64-bit one
+      // 0: float32, 1: BF16, 2: chosen per row (BF16 layers and the 256-row
+      // NVFP4 L2), 3: BF16 with fewer than 2^32 elements in o, so a row's
+      // offset is a 24-bit product (slot < 2^24 as N >= 256), not a 64-bit
+      // one.  The other block-scaled L2s choose once per tile
       auto l2_epilogue = [&](auto modec) __attribute__((always_inline)) {
         constexpr int MODE = decltype(modec)::value;
         const bool o16 = MODE == 2 ? FMT != F_BF16 && LAYER == 2 && p.o_bf16 : MODE == 1 || MODE == 3;
@@ -887,7 +888,7 @@ __global__ void __launch_bounds__(GEMM_THREADS, (TileGeom<FMT, BM>::OCC))
           }
         }
       };
-      // (not the NVFP4 256-row L2, whose registers the second copy overruns)
+      // (the 256-row NVFP4 L2 has no registers to spare for the extra copies)
       if constexpr (FMT != F_BF16 && LAYER == 2 && !(C::NV && BM == 256)) {
         if (p.o_bf16 && p.o_split < (int64_t{1} << 32))
           l2_epilogue(IC<3>{});
