@@ -51,6 +51,13 @@ MULTI = {
 # over to the next tile, so each part fills the copy ring itself).
 TAIL = MoEConfig("bf16_tail", 60, "bf16", 2048, 4096, 512, 8, 2, routing="softmax_uniform")
 TAIL_SHORT = MoEConfig("bf16_tail_short", 60, "bf16", 2048, 6144, 256, 8, 2, routing="softmax_uniform")
+# the guard-band test also covers the split-tail L2's parts buffer and the
+# many-workgroup dispatch (16384 slots) with its scale gather
+GUARD_EXTRA = {
+    "bf16_tail": TAIL,
+    "mxfp8_many": MoEConfig("mxfp8_many", 70, "mxfp8", 2048, 512, 256, 64, 8, routing="softmax_uniform"),
+    "nvfp4_many": MoEConfig("nvfp4_many", 71, "nvfp4", 2048, 512, 256, 64, 8, routing="zipf"),
+}
 
 _CACHE = {}
 
@@ -176,12 +183,13 @@ def test_forward_nvfp4_saturated_l2_input(name):
     compare({**SMALL, **DECODE_SMALL}[name], w2in_scale=1.0 / 64, tag=" saturated")
 
 
-@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small", "mxfp4_decode"])
+@pytest.mark.parametrize("name", ["bf16_small", "mxfp8_small", "mxfp4_small", "nvfp4_small", "mxfp4_decode",
+                                  *GUARD_EXTRA])
 def test_forward_writes_nothing_outside_out_and_workspace(name):
     """Guard bands of a known pattern around ``out`` and the workspace are
     untouched by a forward, and every element of ``out`` is written."""
     from expert_gemms_amd import _lib
-    cfg = {**SMALL, **DECODE_SMALL}[name]
+    cfg = {**SMALL, **DECODE_SMALL, **GUARD_EXTRA}[name]
     x, ids, wts, w = inputs(cfg)
     w2in, _ = l2_scale(cfg)
     _, layer = run_layer(cfg.fmt, x, ids, wts, w, num_shared=cfg.num_shared, w2_input_scale=w2in)
